@@ -1,0 +1,237 @@
+"""fp64 CPU oracle of the Parallax operator -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this module.  The product path (the HIP library and its binding) never
+does, and this module imports nothing from the product path.
+
+What it computes (the Parallax output, eta = 0):
+
+    o_i = o_i^SA - Sigma_KV^(i) rho_i
+
+* o^SA is softmax attention: the write-ups' formula o_PLX = o_SA - Sigma_KV rho
+  ("当注意力学会追问：Parallax如何给Transformer装上第二只眼", section 1.3) and the
+  technical summary ("Riepilogo Tecnico: Parallax ...", section "Meccanismo
+  Principale") define the output as softmax attention minus a KV-covariance
+  correction applied to a per-token probe rho_i.
+* eta, the boundary-amplification factor, is set to zero (same summary,
+  bullet "Rimozione dell'Amplificazione del Confine").
+* Sigma_KV^(i) is written out here as the softmax-weighted covariance
+      Sigma_KV^(i) = sum_j w_ij (v_j - vbar_i)(k_j - kbar_i)^T,
+      w_ij = softmax_j(tau q_i . k_j),  vbar_i = sum_j w_ij v_j,  kbar_i = sum_j w_ij k_j,
+  a d_v x d_k matrix built explicitly for every query.  The pages only call it
+  "the weighted covariance of KV"; the explicit weighted form, with weights
+  that sum to one (a population covariance, no n-1), is the reading used.
+
+Readings where the pages are silent: causal key set j <= i (diagonal
+included) for prefill; a decode query sees all ctx_len[b] cache rows; query
+head h uses KV head floor(h / (Hq / Hkv)); LSE is the natural log-sum-exp of
+the scaled scores; there is no window (the bandwidth is the softmax
+temperature tau).
+
+Backward: the pages give none.  ``row_backward`` is the reverse-mode chain
+rule taken step by step through the explicit forward above (scores ->
+softmax -> moments -> covariance -> output), with rho an independent input.
+
+All arithmetic is float64 on the exact (already dtype-rounded) inputs.  The
+per-row functions only use +, -, *, @ and sums once the weights are known, so
+``row_from_weights`` also runs on numpy object arrays of ``fractions.Fraction``
+for exact-arithmetic checks.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "softmax_weights",
+    "row_from_weights",
+    "row_forward",
+    "prefill_forward",
+    "prefill_rows",
+    "decode_forward",
+    "row_backward",
+    "prefill_backward",
+    "prefill_backward_kv_rows",
+]
+
+
+def softmax_weights(scores: np.ndarray):
+    """w = softmax(scores), and LSE = log sum exp(scores) (natural log)."""
+    m = np.max(scores)
+    e = np.exp(scores - m)
+    z = np.sum(e)
+    return e / z, m + np.log(z)
+
+
+def row_from_weights(w, K, V, rho):
+    """Parallax output of one query given its attention weights.
+
+    w: (n,) weights summing to one; K: (n, d_k); V: (n, d_v); rho: (d_k,).
+    Returns (o, vbar, kbar, Sigma) with Sigma the explicit d_v x d_k weighted
+    KV covariance and o = vbar - Sigma @ rho.
+    """
+    vbar = w @ V
+    kbar = w @ K
+    dv = V - vbar  # rows v_j - vbar
+    dk = K - kbar  # rows k_j - kbar
+    sigma = (dv * w[:, None]).T @ dk  # sum_j w_j (v_j - vbar)(k_j - kbar)^T
+    o = vbar - sigma @ rho
+    return o, vbar, kbar, sigma
+
+
+def row_forward(q, K, V, rho, scale):
+    """One query row: returns (o, o_sa, lse, sigma)."""
+    s = scale * (K @ q)
+    w, lse = softmax_weights(s)
+    o, vbar, _kbar, sigma = row_from_weights(w, K, V, rho)
+    return o, vbar, lse, sigma
+
+
+def _kv_head(h, Hq, Hkv):
+    return h // (Hq // Hkv)
+
+
+def prefill_forward(q, k, v, rho, scale):
+    """Causal prefill.  q, rho: [B, Hq, T, d]; k, v: [B, Hkv, T, d] (float64).
+
+    Returns dict(o, o_sa, lse) with o, o_sa [B, Hq, T, d_v] and lse [B, Hq, T].
+    """
+    B, Hq, T, _ = q.shape
+    Hkv = k.shape[1]
+    dv = v.shape[-1]
+    o = np.empty((B, Hq, T, dv))
+    o_sa = np.empty((B, Hq, T, dv))
+    lse = np.empty((B, Hq, T))
+    for b in range(B):
+        for h in range(Hq):
+            hk = _kv_head(h, Hq, Hkv)
+            for i in range(T):
+                o[b, h, i], o_sa[b, h, i], lse[b, h, i], _ = row_forward(
+                    q[b, h, i], k[b, hk, : i + 1], v[b, hk, : i + 1], rho[b, h, i], scale)
+    return {"o": o, "o_sa": o_sa, "lse": lse}
+
+
+def prefill_rows(get_row, rows, Hq, Hkv, scale):
+    """Causal prefill on sampled rows only.
+
+    ``get_row(b, h, hk, i)`` returns (q_i, K[:i+1], V[:i+1], rho_i) as float64;
+    ``rows`` is an iterable of (b, h, i).  Returns (o, lse) stacked in row order.
+    """
+    outs, lses = [], []
+    for b, h, i in rows:
+        hk = _kv_head(h, Hq, Hkv)
+        qi, K, V, ri = get_row(b, h, hk, i)
+        o, _, lse, _ = row_forward(qi, K, V, ri, scale)
+        outs.append(o)
+        lses.append(lse)
+    return np.array(outs), np.array(lses)
+
+
+def decode_forward(q, rho, k_cache, v_cache, ctx_len, scale, heads=None):
+    """Decode: one query per (b, h) against cache rows [0, ctx_len[b]).
+
+    q, rho: [B, Hq, d]; k_cache, v_cache: [B, Hkv, S_max, d] (float64 or a
+    callable ``kv(b, hk, n) -> (K, V)``).  ``heads`` optionally restricts the
+    work to a list of (b, h).  Returns dict(o, lse) over the requested heads.
+    """
+    B, Hq, _ = q.shape
+    if callable(k_cache):
+        Hkv = v_cache
+        fetch = k_cache
+    else:
+        Hkv = k_cache.shape[1]
+
+        def fetch(b, hk, n):
+            return k_cache[b, hk, :n], v_cache[b, hk, :n]
+
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(Hq)]
+    o, lse = [], []
+    for b, h in heads:
+        hk = _kv_head(h, Hq, Hkv)
+        K, V = fetch(b, hk, int(ctx_len[b]))
+        ob, _, lb, _ = row_forward(q[b, h], K, V, rho[b, h], scale)
+        o.append(ob)
+        lse.append(lb)
+    return {"o": np.array(o), "lse": np.array(lse), "heads": heads}
+
+
+def row_backward(q, K, V, rho, g, scale):
+    """Gradients of <g, o> for one query row, by reverse mode through the
+    explicit forward.  Returns (dq, dK, dV, drho) with dK, dV shaped like K, V.
+    """
+    n = K.shape[0]
+    # forward, keeping every intermediate
+    s = scale * (K @ q)
+    w, _ = softmax_weights(s)
+    vbar = w @ V
+    kbar = w @ K
+    a = V - vbar  # a_j = v_j - vbar
+    bk = K - kbar  # b_j = k_j - kbar
+    sigma = (a * w[:, None]).T @ bk
+    # o = vbar - sigma @ rho
+    d_vbar = g.copy()
+    d_sigma = -np.outer(g, rho)
+    d_rho = -sigma.T @ g
+    # sigma = sum_j w_j a_j b_j^T
+    a_ds = a @ d_sigma  # row j: a_j^T dSigma
+    d_w = np.sum(a_ds * bk, axis=1)  # a_j^T dSigma b_j
+    d_a = w[:, None] * (bk @ d_sigma.T)  # w_j dSigma b_j
+    d_b = w[:, None] * a_ds  # w_j dSigma^T a_j
+    dV = d_a.copy()
+    dK = d_b.copy()
+    d_vbar = d_vbar - d_a.sum(axis=0)  # a_j = v_j - vbar
+    d_kbar = -d_b.sum(axis=0)  # b_j = k_j - kbar
+    # vbar = sum_j w_j v_j ; kbar = sum_j w_j k_j
+    d_w = d_w + V @ d_vbar + K @ d_kbar
+    dV += np.outer(w, d_vbar)
+    dK += np.outer(w, d_kbar)
+    # w = softmax(s)
+    d_s = w * (d_w - np.dot(w, d_w))
+    # s = scale * K q
+    dq = scale * (d_s @ K)
+    dK += scale * np.outer(d_s, q)
+    assert dK.shape == (n, K.shape[1])
+    return dq, dK, dV, d_rho
+
+
+def prefill_backward(q, k, v, rho, d_o, scale):
+    """Full causal backward.  Returns dict(dq, dk, dv, drho), GQA K/V gradients
+    summed over the query heads that share a KV head."""
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    dq = np.zeros_like(q)
+    drho = np.zeros_like(rho)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            hk = _kv_head(h, Hq, Hkv)
+            for i in range(T):
+                gq, gK, gV, gr = row_backward(q[b, h, i], k[b, hk, : i + 1], v[b, hk, : i + 1],
+                                              rho[b, h, i], d_o[b, h, i], scale)
+                dq[b, h, i] = gq
+                drho[b, h, i] = gr
+                dk[b, hk, : i + 1] += gK
+                dv[b, hk, : i + 1] += gV
+    return {"dq": dq, "dk": dk, "dv": dv, "drho": drho}
+
+
+def prefill_backward_kv_rows(get_row, keys, T, Hq, Hkv, scale):
+    """dK and dV of sampled keys (b, hk, j): sums over every query row i >= j of
+    every query head of the group.  ``get_row(b, h, hk, i)`` returns
+    (q_i, K[:i+1], V[:i+1], rho_i, g_i) as float64.  Returns (dk, dv) stacked."""
+    group = Hq // Hkv
+    dks, dvs = [], []
+    for b, hk, j in keys:
+        acc_k = None
+        acc_v = None
+        for h in range(hk * group, (hk + 1) * group):
+            for i in range(j, T):
+                qi, K, V, ri, gi = get_row(b, h, hk, i)
+                _, gK, gV, _ = row_backward(qi, K, V, ri, gi, scale)
+                acc_k = gK[j] if acc_k is None else acc_k + gK[j]
+                acc_v = gV[j] if acc_v is None else acc_v + gV[j]
+        dks.append(acc_k)
+        dvs.append(acc_v)
+    return np.array(dks), np.array(dvs)
