@@ -1,0 +1,162 @@
+/*
+ * plx.h -- C ABI of the Parallax attention library for AMD MI355X (gfx950).
+ *
+ * The operator (parameterized Local Linear Attention, boundary factor eta = 0):
+ *
+ *     o_i = o_i^SA - Sigma_KV^(i) rho_i
+ *
+ *   o^SA          causal softmax attention with scale tau (usually 1/sqrt(d));
+ *   Sigma_KV^(i)  sum_j w_ij (v_j - vbar_i)(k_j - kbar_i)^T, the softmax-weighted
+ *                 KV covariance, w_ij = softmax_j(tau q_i . k_j),
+ *                 vbar_i = sum_j w_ij v_j, kbar_i = sum_j w_ij k_j;
+ *   rho_i         the per-token probe (a learned projection W_R x_i computed by
+ *                 the caller, outside this library).
+ *
+ * Sources: "当注意力学会追问：Parallax如何给Transformer装上第二只眼" (zhichai.net),
+ * section 1.3, formula o_i^PLX = o_i^SA - Sigma_KV^(i) rho_i with rho_i = W_R x_i;
+ * "Riepilogo Tecnico: Parallax ..." (gist.science), section "Meccanismo
+ * Principale" (same formula; eta_i set to zero) and section "Algoritmo
+ * Consapevole dell'Hardware" (one streaming pass reusing the KV stream, QK and
+ * RK in the same matrix instructions, a custom decode kernel).  The pages call
+ * Sigma_KV only "the KV covariance"; the explicit weighted form above is the
+ * reading this library implements.
+ *
+ * Conventions shared by every entry point
+ *   - Layout: dense, contiguous [B, H, T, d] (d fastest).  K and V use Hkv heads,
+ *     q / rho / dO use Hq heads; query head h reads KV head h / (Hq / Hkv).
+ *   - dtype applies to q, k, v, rho and dO: PLX_BF16 (bf16 storage; score GEMMs in
+ *     bf16 MFMA with fp32 accumulation, softmax-weighted GEMMs with fp16 operands
+ *     and fp32 accumulation) or PLX_F32 (fp32 throughout).  Every output (o, LSE,
+ *     auxiliaries, gradients) is fp32.
+ *   - Supported head dims: d = 64 or 128 (d_k = d_v = d).
+ *   - All pointers are DEVICE pointers unless stated.  The caller owns every
+ *     buffer; the library never allocates or frees device memory and keeps no
+ *     state between calls.  Calls are asynchronous on `stream` (a hipStream_t;
+ *     NULL is the default stream); device faults surface at the caller's sync.
+ *   - Errors: arguments are validated before any HIP call.  Bad pointers / sizes
+ *     return PLX_ERR_INVALID_ARG, valid but unsupported shapes return
+ *     PLX_ERR_UNSUPPORTED, a short workspace returns PLX_ERR_WORKSPACE, a failed
+ *     launch returns PLX_ERR_HIP.  Nothing is launched when an error is returned.
+ *   - Thread-safe: no global mutable state.
+ */
+#ifndef PLX_H_
+#define PLX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PLX_OK = 0,
+  PLX_ERR_INVALID_ARG = 1,
+  PLX_ERR_UNSUPPORTED = 2,
+  PLX_ERR_WORKSPACE = 3,
+  PLX_ERR_HIP = 4
+} plx_status;
+
+typedef enum { PLX_F32 = 0, PLX_BF16 = 1 } plx_dtype;
+
+/* Opaque stream handle; pass a hipStream_t (or NULL for the default stream). */
+typedef void* plx_stream;
+
+/* ABI version of this header (incremented on incompatible changes). */
+#define PLX_ABI_VERSION 1
+int plx_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* plx_status_string(plx_status s);
+
+/*
+ * Causal prefill forward.
+ *
+ * Computes, for every (b, h, i) with keys j <= i (diagonal included),
+ *   o[b,h,i,:] = vbar_i - Sigma_KV^(i) rho_i  (fp32),
+ * in one streaming pass that carries the online-softmax max and sum with the
+ * accumulators O = P V, U = (P . R) V and C = rowsum(P . R), R = rho K^T, and
+ * ends with o = (O/l)(1 + C/l) - U/l (the identity
+ * Sigma_KV rho = sum_j w_j (k_j . rho) v_j - vbar (kbar . rho)).
+ *
+ *   q, rho      [B, Hq, T, d]   dtype
+ *   k, v        [B, Hkv, T, d]  dtype
+ *   o           [B, Hq, T, d]   fp32, written
+ *   lse         [B, Hq, T]      fp32 natural log-sum-exp of tau q.k, or NULL
+ *   c_aux       [B, Hq, T]      fp32 c_i = kbar_i . rho_i, or NULL
+ *   vbar_aux    [B, Hq, T, d]   fp32 vbar_i (the softmax-attention output), or NULL
+ *   scale       tau > 0 (finite)
+ * lse, c_aux and vbar_aux are the auxiliaries plx_bwd needs.
+ * Requires B, Hq, Hkv, T >= 1, Hq % Hkv == 0, d in {64, 128}, 16-byte aligned
+ * pointers.  A T that is not a multiple of any tile size is handled exactly.
+ */
+plx_status plx_fwd_prefill(const void* q, const void* k, const void* v, const void* rho,
+                           float* o, float* lse, float* c_aux, float* vbar_aux,
+                           int B, int Hq, int Hkv, int T, int d, float scale,
+                           plx_dtype dtype, plx_stream stream);
+
+/*
+ * Decode: one new query and probe per (b, h) against a KV cache.
+ *
+ * Query (b, h) attends to the cache rows [0, ctx_len[b]) of KV head h/(Hq/Hkv)
+ * (the cache already holds the current token; no mask).  The key range of every
+ * sequence is cut into splits processed by separate workgroups, each producing a
+ * partial record (m, l, O, U, Kbar) -- running max, sum, P V, (P . R) V and P K --
+ * which a second kernel merges:
+ *   M = max m_s, a_s = exp(m_s - M), l = sum a_s l_s, O/U/Kbar likewise,
+ *   o = (O/l)(1 + (Kbar . rho)/l) - U/l,   LSE = M + ln l.
+ *
+ *   q, rho        [B, Hq, d]          dtype
+ *   k_cache       [B, Hkv, S_max, d]  dtype
+ *   v_cache       [B, Hkv, S_max, d]  dtype
+ *   ctx_len       [B] int32, DEVICE memory, read by the kernels.  A value outside
+ *                 [1, S_max] makes that sequence's o and lse NaN (no out-of-range
+ *                 cache row is ever read).
+ *   o             [B, Hq, d] fp32, written
+ *   lse           [B, Hq] fp32, or NULL
+ *   num_splits    number of key splits over S_max, 0 = automatic
+ *   workspace     device scratch of at least plx_decode_workspace_size(...) bytes,
+ *                 16-byte aligned; contents on entry are ignored
+ * Requires group = Hq / Hkv in {1, 2, 4, 8, 16}.  Rows of the cache at or beyond
+ * ctx_len[b] are never read.
+ */
+size_t plx_decode_workspace_size(int B, int Hq, int Hkv, int S_max, int d, int num_splits);
+plx_status plx_decode(const void* q, const void* rho, const void* k_cache, const void* v_cache,
+                      const int32_t* ctx_len, float* o, float* lse,
+                      int B, int Hq, int Hkv, int S_max, int d, float scale, int num_splits,
+                      void* workspace, size_t workspace_bytes, plx_dtype dtype, plx_stream stream);
+
+/*
+ * Backward of the causal prefill (the pages give none; these are the exact
+ * gradients of the forward above with rho an independent input).
+ *
+ * With g = dO_i, A_ij = g . v_j, G_i = g . o_i, delta_i = g . vbar_i,
+ * c_i = kbar_i . rho_i, r_ij = rho_i . k_j and w_ij recomputed from the saved LSE:
+ *   dV_j   = sum_i w_ij (1 + c_i - r_ij) g_i
+ *   dS_ij  = w_ij [ (1 + c_i - r_ij) A_ij - G_i + delta_i (r_ij - c_i) ]
+ *   dR_ij  = -w_ij (A_ij - delta_i)
+ *   dQ = tau dS K,  dK = tau dS^T Q + dR^T rho,  drho = dR K.
+ * dK and dV sum over the query heads that share a KV head.
+ *
+ *   q, rho, dO  [B, Hq, T, d]  dtype      k, v  [B, Hkv, T, d]  dtype
+ *   o           [B, Hq, T, d]  fp32 (forward output)
+ *   lse, c_aux  [B, Hq, T]     fp32 (forward auxiliaries, required)
+ *   vbar_aux    [B, Hq, T, d]  fp32 (forward auxiliary, required)
+ *   dq, drho    [B, Hq, T, d]  fp32, written (overwritten, not accumulated)
+ *   dk, dv      [B, Hkv, T, d] fp32, written (overwritten, not accumulated)
+ *   workspace   at least plx_bwd_workspace_size(...) bytes, 16-byte aligned
+ * The result is deterministic (no atomics): one kernel owns each key block and
+ * one kernel owns each query block.
+ */
+size_t plx_bwd_workspace_size(int B, int Hq, int Hkv, int T, int d);
+plx_status plx_bwd(const void* q, const void* k, const void* v, const void* rho, const void* d_o,
+                   const float* o, const float* lse, const float* c_aux, const float* vbar_aux,
+                   float* dq, float* dk, float* dv, float* drho,
+                   int B, int Hq, int Hkv, int T, int d, float scale,
+                   void* workspace, size_t workspace_bytes, plx_dtype dtype, plx_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PLX_H_ */

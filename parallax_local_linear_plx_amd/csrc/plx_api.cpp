@@ -1,0 +1,121 @@
+// C-ABI layer: argument validation (before any HIP call) and dispatch.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "plx.h"
+#include "plx_kernels.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_ok(plx_dtype dt) { return dt == PLX_F32 || dt == PLX_BF16; }
+
+plx_status check_heads(int B, int Hq, int Hkv, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1) return PLX_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return PLX_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return PLX_ERR_UNSUPPORTED;
+  return PLX_OK;
+}
+
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+plx_status from_hip(hipError_t e) { return e == hipSuccess ? PLX_OK : PLX_ERR_HIP; }
+
+// Element counts must stay addressable with 32-bit row indices times d.
+bool size_ok(long long rows, int d) { return rows > 0 && rows * (long long)d < (1LL << 40); }
+
+}  // namespace
+
+extern "C" {
+
+int plx_abi_version(void) { return PLX_ABI_VERSION; }
+
+const char* plx_status_string(plx_status s) {
+  switch (s) {
+    case PLX_OK: return "ok";
+    case PLX_ERR_INVALID_ARG: return "invalid argument";
+    case PLX_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PLX_ERR_WORKSPACE: return "workspace too small";
+    case PLX_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+plx_status plx_fwd_prefill(const void* q, const void* k, const void* v, const void* rho, float* o,
+                           float* lse, float* c_aux, float* vbar_aux, int B, int Hq, int Hkv, int T,
+                           int d, float scale, plx_dtype dtype, plx_stream stream) {
+  if (!q || !k || !v || !rho || !o) return PLX_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype) || T < 1 || !scale_ok(scale)) return PLX_ERR_INVALID_ARG;
+  plx_status st = check_heads(B, Hq, Hkv, d);
+  if (st != PLX_OK) return st;
+  if (!size_ok((long long)B * Hq * T, d)) return PLX_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rho) || !aligned16(o) ||
+      (vbar_aux && !aligned16(vbar_aux)))
+    return PLX_ERR_INVALID_ARG;
+  return from_hip(plx::launch_fwd(dtype, q, k, v, rho, o, lse, c_aux, vbar_aux, B, Hq, Hkv, T, d,
+                                  scale, (hipStream_t)stream));
+}
+
+size_t plx_decode_workspace_size(int B, int Hq, int Hkv, int S_max, int d, int num_splits) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || S_max < 1 || num_splits < 0) return 0;
+  if (d != 64 && d != 128) return 0;
+  int ns = num_splits > 0 ? num_splits : plx::decode_auto_splits(B, Hkv, S_max);
+  if (ns > S_max) ns = S_max;
+  const int chunk = plx::decode_chunk_keys(S_max, ns);
+  ns = (S_max + chunk - 1) / chunk;
+  return (size_t)B * Hq * ns * plx::decode_record_floats(d) * sizeof(float);
+}
+
+plx_status plx_decode(const void* q, const void* rho, const void* k_cache, const void* v_cache,
+                      const int32_t* ctx_len, float* o, float* lse, int B, int Hq, int Hkv,
+                      int S_max, int d, float scale, int num_splits, void* workspace,
+                      size_t workspace_bytes, plx_dtype dtype, plx_stream stream) {
+  if (!q || !rho || !k_cache || !v_cache || !ctx_len || !o) return PLX_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype) || S_max < 1 || num_splits < 0 || !scale_ok(scale)) return PLX_ERR_INVALID_ARG;
+  plx_status st = check_heads(B, Hq, Hkv, d);
+  if (st != PLX_OK) return st;
+  const int group = Hq / Hkv;
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return PLX_ERR_UNSUPPORTED;
+  if (!size_ok((long long)B * Hkv * S_max, d)) return PLX_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(rho) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(o) || (workspace && !aligned16(workspace)))
+    return PLX_ERR_INVALID_ARG;
+  const size_t need = plx_decode_workspace_size(B, Hq, Hkv, S_max, d, num_splits);
+  if (!workspace || workspace_bytes < need) return PLX_ERR_WORKSPACE;
+  return from_hip(plx::launch_decode(dtype, q, rho, k_cache, v_cache, ctx_len, o, lse, B, Hq, Hkv,
+                                     S_max, d, scale, num_splits, (float*)workspace,
+                                     (hipStream_t)stream));
+}
+
+size_t plx_bwd_workspace_size(int B, int Hq, int Hkv, int T, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || T < 1) return 0;
+  if (d != 64 && d != 128) return 0;
+  // G_i = dO_i . o_i and delta_i = dO_i . vbar_i, fp32 each
+  return (size_t)2 * B * Hq * T * sizeof(float);
+}
+
+plx_status plx_bwd(const void* q, const void* k, const void* v, const void* rho, const void* d_o,
+                   const float* o, const float* lse, const float* c_aux, const float* vbar_aux,
+                   float* dq, float* dk, float* dv, float* drho, int B, int Hq, int Hkv, int T, int d,
+                   float scale, void* workspace, size_t workspace_bytes, plx_dtype dtype,
+                   plx_stream stream) {
+  if (!q || !k || !v || !rho || !d_o || !o || !lse || !c_aux || !vbar_aux) return PLX_ERR_INVALID_ARG;
+  if (!dq || !dk || !dv || !drho) return PLX_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype) || T < 1 || !scale_ok(scale)) return PLX_ERR_INVALID_ARG;
+  plx_status st = check_heads(B, Hq, Hkv, d);
+  if (st != PLX_OK) return st;
+  if (!size_ok((long long)B * Hq * T, d)) return PLX_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, rho, d_o, o, vbar_aux, dq, dk, dv, drho};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return PLX_ERR_INVALID_ARG;
+  const size_t need = plx_bwd_workspace_size(B, Hq, Hkv, T, d);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return PLX_ERR_WORKSPACE;
+  return from_hip(plx::launch_bwd(dtype, q, k, v, rho, d_o, o, lse, c_aux, vbar_aux, dq, dk, dv,
+                                  drho, B, Hq, Hkv, T, d, scale, (float*)workspace,
+                                  (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,430 @@
+// Backward of the causal Parallax prefill.
+//
+// The write-ups give no backward pass; these are the exact gradients of the
+// forward with the probe rho an independent input.  Per query row i, with
+// g = dO_i, the recomputed weights w_ij = exp(tau q_i.k_j - LSE_i),
+// r_ij = rho_i . k_j, A_ij = g . v_j, G_i = g . o_i, delta_i = g . vbar_i and
+// c_i = kbar_i . rho_i (so o_i = sum_j w_ij (1 + c_i - r_ij) v_j):
+//   dV_j  = sum_i w_ij (1 + c_i - r_ij) g_i
+//   dS_ij = w_ij [ (1 + c_i - r_ij) A_ij - G_i + delta_i (r_ij - c_i) ]
+//   dR_ij = -w_ij (A_ij - delta_i)
+//   dQ = tau dS K,  dK = tau dS^T Q + dR^T rho,  drho = dR K.
+//
+// Three kernels, no atomics (the result is deterministic):
+//   pre   : G and delta per row.
+//   dq    : query-outer, laid out like the forward (S^T = K Q^T, one query per
+//           lane column): recomputes S, R and A^T = V dO^T per key tile, forms
+//           dS, dR in registers and accumulates dQ^T = K^T dS^T, drho^T = K^T dR^T.
+//   dkdv  : key-outer: one key per lane column (S = Q K^T), loops over the
+//           query tiles of every head that shares the KV head, accumulates
+//           dV^T = dO^T Ptilde and dK^T = Q^T (tau dS) + rho^T dR.
+#include "plx_common.hpp"
+#include "plx_kernels.hpp"
+
+namespace plx {
+
+namespace {
+
+constexpr int BWD_THREADS = 256;
+
+// ---------------------------------------------------------------- preprocess
+template <class Pol, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const typename Pol::in_t* __restrict__ d_o,
+                                                     const float* __restrict__ o,
+                                                     const float* __restrict__ vbar,
+                                                     float* __restrict__ G, float* __restrict__ delta,
+                                                     long long rows) {
+  constexpr int PER = D / 16;  // elements per thread, 16 threads per row
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int t = threadIdx.x & 15;
+  float g = 0.f, dl = 0.f;
+  if (row < rows) {
+    const size_t base = (size_t)row * D + t * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float x = Pol::to_f32(d_o[base + e]);
+      g += x * o[base + e];
+      dl += x * vbar[base + e];
+    }
+  }
+#pragma unroll
+  for (int off = 8; off > 0; off >>= 1) {
+    g += __shfl_xor(g, off, 16);
+    dl += __shfl_xor(dl, off, 16);
+  }
+  if (row < rows && t == 0) {
+    G[row] = g;
+    delta[row] = dl;
+  }
+}
+
+// ------------------------------------------------------------- dQ and drho
+constexpr int DQ_BR = 128;
+constexpr int DQ_BC = 64;
+
+template <class Pol, int D>
+struct DqSmem {
+  using in_t = typename Pol::in_t;
+  using vel_t = typename Pol::vel_t;
+  static constexpr int LD = D + 16 / sizeof(in_t);
+  static constexpr int TLD = DQ_BC + 4;
+  in_t k[DQ_BC * LD];
+  in_t v[DQ_BC * LD];
+  vel_t kt[D * TLD];
+};
+
+template <class Pol, int D>
+__global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq_kernel(
+    const typename Pol::in_t* __restrict__ q, const typename Pol::in_t* __restrict__ k,
+    const typename Pol::in_t* __restrict__ v, const typename Pol::in_t* __restrict__ rho,
+    const typename Pol::in_t* __restrict__ d_o, const float* __restrict__ lse,
+    const float* __restrict__ c_aux, const float* __restrict__ Gv, const float* __restrict__ dlt,
+    float* __restrict__ dq, float* __restrict__ drho, int B, int Hq, int Hkv, int T, float scale,
+    float scale_log2) {
+  using in_t = typename Pol::in_t;
+  using sop_t = typename Pol::sop_t;
+  using vop_t = typename Pol::vop_t;
+  constexpr int KW = Pol::KW, KSTEP = Pol::KSTEP;
+  constexpr int NS = D / KSTEP, NV = 32 / KSTEP, ND = D / 32;
+  using SM = DqSmem<Pol, D>;
+  __shared__ SM sm;
+
+  const int nqb = (T + DQ_BR - 1) / DQ_BR;
+  const int bh_count = B * Hq;
+  const int lin = blockIdx.x;
+  const int qb = nqb - 1 - lin / bh_count;
+  const int bh = lin % bh_count;
+  const int b = bh / Hq, h = bh % Hq;
+  const int hk = h / (Hq / Hkv);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int q0 = qb * DQ_BR;
+  const int qw = q0 + 32 * wave;
+  const int my_q = qw + col;
+  const bool qvalid = my_q < T;
+
+  const size_t rowbase = (size_t)bh * T;
+  sop_t qop[NS], rop[NS], gop[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (qvalid) {
+      const size_t off = (rowbase + my_q) * D + KSTEP * s + KW * half;
+      qop[s] = load_sop<Pol>(q + off);
+      rop[s] = load_sop<Pol>(rho + off);
+      gop[s] = load_sop<Pol>(d_o + off);
+    } else {
+      qop[s] = rop[s] = gop[s] = zero_sop<Pol>();
+    }
+  }
+  const float lse2 = qvalid ? lse[rowbase + my_q] * kLog2e : 0.f;
+  const float ci = qvalid ? c_aux[rowbase + my_q] : 0.f;
+  const float Gi = qvalid ? Gv[rowbase + my_q] : 0.f;
+  const float di = qvalid ? dlt[rowbase + my_q] : 0.f;
+
+  f32x16 dqa[ND], dra[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    dqa[i] = zero16();
+    dra[i] = zero16();
+  }
+
+  const in_t* kp = k + ((size_t)(b * Hkv + hk) * T) * D;
+  const in_t* vp = v + ((size_t)(b * Hkv + hk) * T) * D;
+  const int kend = min(T, q0 + DQ_BR);
+  const int ntiles = (kend + DQ_BC - 1) / DQ_BC;
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int key0 = j * DQ_BC;
+    const int nvalid = min(DQ_BC, T - key0);
+    __syncthreads();
+    stage_rows<Pol, D, DQ_BC, BWD_THREADS>(sm.k, SM::LD, kp + (size_t)key0 * D, nvalid);
+    stage_rows<Pol, D, DQ_BC, BWD_THREADS>(sm.v, SM::LD, vp + (size_t)key0 * D, nvalid);
+    stage_rows_t<Pol, D, DQ_BC, BWD_THREADS>(sm.kt, SM::TLD, kp + (size_t)key0 * D, nvalid);
+    __syncthreads();
+    if (key0 > qw + 31) continue;
+
+    f32x16 sa[2], ra[2], aa[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      sa[st] = ra[st] = aa[st] = zero16();
+      const in_t* krow = &sm.k[(32 * st + col) * SM::LD + KW * half];
+      const in_t* vrow = &sm.v[(32 * st + col) * SM::LD + KW * half];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const sop_t ak = load_sop<Pol>(krow + KSTEP * s);
+        const sop_t av = load_sop<Pol>(vrow + KSTEP * s);
+        sa[st] = Pol::mma_s(ak, qop[s], sa[st]);
+        ra[st] = Pol::mma_s(ak, rop[s], ra[st]);
+        aa[st] = Pol::mma_s(av, gop[s], aa[st]);
+      }
+    }
+    // dS^T and dR^T in place of S^T and R^T
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const int key = key0 + 32 * st + acc_row(a, half);
+        float p = fast_exp2(__builtin_fmaf(sa[st][a], scale_log2, -lse2));
+        if (key > my_q || !qvalid) p = 0.f;
+        const float r = ra[st][a], A = aa[st][a];
+        const float f = 1.f + ci - r;
+        sa[st][a] = p * (f * A - Gi + di * (r - ci));
+        ra[st][a] = -p * (A - di);
+      }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int s = 0; s < NV; ++s) {
+        vop_t dsop, drop;
+#pragma unroll
+        for (int e = 0; e < KW; ++e) {
+          set_elem(dsop, e, Pol::round_v(sa[st][KW * s + e]));
+          set_elem(drop, e, Pol::round_v(ra[st][KW * s + e]));
+        }
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+          const vop_t a = load_t_op<Pol>(sm.kt, SM::TLD, 32 * dt + col, 32 * st, s, half);
+          dqa[dt] = Pol::mma_v(a, dsop, dqa[dt]);
+          dra[dt] = Pol::mma_v(a, drop, dra[dt]);
+        }
+      }
+  }
+
+  if (qvalid) {
+    float* dqr = dq + (rowbase + my_q) * D;
+    float* drr = drho + (rowbase + my_q) * D;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * dt + 8 * i + 4 * half;
+        f32x4 x, y;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          x[jj] = scale * dqa[dt][4 * i + jj];
+          y[jj] = dra[dt][4 * i + jj];
+        }
+        *reinterpret_cast<f32x4*>(dqr + d0) = x;
+        *reinterpret_cast<f32x4*>(drr + d0) = y;
+      }
+  }
+}
+
+// --------------------------------------------------------------- dK and dV
+constexpr int KV_BK = 128;  // keys per workgroup (32 per wave)
+constexpr int KV_BQ = 64;   // queries per LDS tile
+
+template <class Pol, int D>
+struct DkvSmem {
+  using in_t = typename Pol::in_t;
+  using vel_t = typename Pol::vel_t;
+  static constexpr int LD = D + 16 / sizeof(in_t);
+  static constexpr int TLD = KV_BQ + 4;
+  in_t q[KV_BQ * LD];
+  in_t r[KV_BQ * LD];
+  in_t g[KV_BQ * LD];
+  vel_t qt[D * TLD];
+  vel_t rt[D * TLD];
+  vel_t gt[D * TLD];
+  float lse2[KV_BQ];
+  float c[KV_BQ];
+  float G[KV_BQ];
+  float dl[KV_BQ];
+};
+
+template <class Pol, int D>
+__global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv_kernel(
+    const typename Pol::in_t* __restrict__ q, const typename Pol::in_t* __restrict__ k,
+    const typename Pol::in_t* __restrict__ v, const typename Pol::in_t* __restrict__ rho,
+    const typename Pol::in_t* __restrict__ d_o, const float* __restrict__ lse,
+    const float* __restrict__ c_aux, const float* __restrict__ Gv, const float* __restrict__ dlt,
+    float* __restrict__ dk, float* __restrict__ dv, int B, int Hq, int Hkv, int T, float scale,
+    float scale_log2) {
+  using in_t = typename Pol::in_t;
+  using sop_t = typename Pol::sop_t;
+  using vop_t = typename Pol::vop_t;
+  constexpr int KW = Pol::KW, KSTEP = Pol::KSTEP;
+  constexpr int NS = D / KSTEP, NV = 32 / KSTEP, ND = D / 32;
+  using SM = DkvSmem<Pol, D>;
+  __shared__ SM sm;
+
+  const int bhk_count = B * Hkv;
+  const int lin = blockIdx.x;
+  const int kb = lin / bhk_count;  // ascending: early key blocks see the most queries
+  const int bhk = lin % bhk_count;
+  const int b = bhk / Hkv, hk = bhk % Hkv;
+  const int G = Hq / Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int k0 = kb * KV_BK;
+  const int kw = k0 + 32 * wave;
+  const int my_k = kw + col;
+  const bool kvalid = my_k < T;
+
+  const size_t kvbase = (size_t)bhk * T;
+  sop_t kop[NS], vop[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    if (kvalid) {
+      const size_t off = (kvbase + my_k) * D + KSTEP * s + KW * half;
+      kop[s] = load_sop<Pol>(k + off);
+      vop[s] = load_sop<Pol>(v + off);
+    } else {
+      kop[s] = vop[s] = zero_sop<Pol>();
+    }
+  }
+
+  f32x16 dka[ND], dva[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    dka[i] = zero16();
+    dva[i] = zero16();
+  }
+
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = hk * G + hh;
+    const size_t rowbase = ((size_t)b * Hq + h) * T;
+    for (int qt0 = k0; qt0 < T; qt0 += KV_BQ) {
+      const int nvalid = min(KV_BQ, T - qt0);
+      __syncthreads();
+      stage_rows<Pol, D, KV_BQ, BWD_THREADS>(sm.q, SM::LD, q + (rowbase + qt0) * D, nvalid);
+      stage_rows<Pol, D, KV_BQ, BWD_THREADS>(sm.r, SM::LD, rho + (rowbase + qt0) * D, nvalid);
+      stage_rows<Pol, D, KV_BQ, BWD_THREADS>(sm.g, SM::LD, d_o + (rowbase + qt0) * D, nvalid);
+      stage_rows_t<Pol, D, KV_BQ, BWD_THREADS>(sm.qt, SM::TLD, q + (rowbase + qt0) * D, nvalid);
+      stage_rows_t<Pol, D, KV_BQ, BWD_THREADS>(sm.rt, SM::TLD, rho + (rowbase + qt0) * D, nvalid);
+      stage_rows_t<Pol, D, KV_BQ, BWD_THREADS>(sm.gt, SM::TLD, d_o + (rowbase + qt0) * D, nvalid);
+      if (threadIdx.x < KV_BQ) {
+        const int i = threadIdx.x;
+        const bool ok = i < nvalid;
+        sm.lse2[i] = ok ? lse[rowbase + qt0 + i] * kLog2e : 0.f;
+        sm.c[i] = ok ? c_aux[rowbase + qt0 + i] : 0.f;
+        sm.G[i] = ok ? Gv[rowbase + qt0 + i] : 0.f;
+        sm.dl[i] = ok ? dlt[rowbase + qt0 + i] : 0.f;
+      }
+      __syncthreads();
+
+#pragma unroll
+      for (int st = 0; st < KV_BQ / 32; ++st) {
+        const int qs = qt0 + 32 * st;
+        if (qs + 31 < kw) continue;  // every query of the sub-tile precedes every key of the wave
+        f32x16 sa = zero16(), ra = zero16(), aa = zero16();
+        const in_t* qrow = &sm.q[(32 * st + col) * SM::LD + KW * half];
+        const in_t* rrow = &sm.r[(32 * st + col) * SM::LD + KW * half];
+        const in_t* grow = &sm.g[(32 * st + col) * SM::LD + KW * half];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          sa = Pol::mma_s(load_sop<Pol>(qrow + KSTEP * s), kop[s], sa);
+          ra = Pol::mma_s(load_sop<Pol>(rrow + KSTEP * s), kop[s], ra);
+          aa = Pol::mma_s(load_sop<Pol>(grow + KSTEP * s), vop[s], aa);
+        }
+        // lane column = key my_k; accumulator slot a = query qs + acc_row(a, half)
+        float pt[16], ds[16], dr[16];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int r0 = 32 * st + 8 * i4 + 4 * half;  // local query of slot 4*i4
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[r0]);
+          const f32x4 c4 = *reinterpret_cast<const f32x4*>(&sm.c[r0]);
+          const f32x4 g4 = *reinterpret_cast<const f32x4*>(&sm.G[r0]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dl[r0]);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int a = 4 * i4 + jj;
+            const int qi = qt0 + r0 + jj;
+            float p = fast_exp2(__builtin_fmaf(sa[a], scale_log2, -l4[jj]));
+            if (qi < my_k || qi >= T) p = 0.f;
+            const float r = ra[a], A = aa[a];
+            const float f = 1.f + c4[jj] - r;
+            pt[a] = p * f;
+            ds[a] = scale * p * (f * A - g4[jj] + d4[jj] * (r - c4[jj]));
+            dr[a] = -p * (A - d4[jj]);
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < NV; ++s) {
+          vop_t pop, dsop, drop;
+#pragma unroll
+          for (int e = 0; e < KW; ++e) {
+            set_elem(pop, e, Pol::round_v(pt[KW * s + e]));
+            set_elem(dsop, e, Pol::round_v(ds[KW * s + e]));
+            set_elem(drop, e, Pol::round_v(dr[KW * s + e]));
+          }
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) {
+            const int drow = 32 * dt + col;
+            const vop_t ag = load_t_op<Pol>(sm.gt, SM::TLD, drow, 32 * st, s, half);
+            const vop_t aq = load_t_op<Pol>(sm.qt, SM::TLD, drow, 32 * st, s, half);
+            const vop_t ar = load_t_op<Pol>(sm.rt, SM::TLD, drow, 32 * st, s, half);
+            dva[dt] = Pol::mma_v(ag, pop, dva[dt]);
+            dka[dt] = Pol::mma_v(aq, dsop, dka[dt]);
+            dka[dt] = Pol::mma_v(ar, drop, dka[dt]);
+          }
+        }
+      }
+    }
+  }
+
+  if (kvalid) {
+    float* dkr = dk + (kvbase + my_k) * D;
+    float* dvr = dv + (kvbase + my_k) * D;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * dt + 8 * i + 4 * half;
+        f32x4 x, y;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          x[jj] = dka[dt][4 * i + jj];
+          y[jj] = dva[dt][4 * i + jj];
+        }
+        *reinterpret_cast<f32x4*>(dkr + d0) = x;
+        *reinterpret_cast<f32x4*>(dvr + d0) = y;
+      }
+  }
+}
+
+template <class Pol, int D>
+hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* rho,
+                        const void* d_o, const float* o, const float* lse, const float* c_aux,
+                        const float* vbar, float* dq, float* dk, float* dv, float* drho, int B,
+                        int Hq, int Hkv, int T, float scale, float* ws, hipStream_t stream) {
+  using in_t = typename Pol::in_t;
+  const long long rows = (long long)B * Hq * T;
+  float* G = ws;
+  float* dl = ws + rows;
+  hipLaunchKernelGGL((bwd_pre_kernel<Pol, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
+                     stream, (const in_t*)d_o, o, vbar, G, dl, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqb = (T + DQ_BR - 1) / DQ_BR;
+  hipLaunchKernelGGL((bwd_dq_kernel<Pol, D>), dim3(nqb * B * Hq), dim3(BWD_THREADS), 0, stream,
+                     (const in_t*)q, (const in_t*)k, (const in_t*)v, (const in_t*)rho,
+                     (const in_t*)d_o, lse, c_aux, G, dl, dq, drho, B, Hq, Hkv, T, scale,
+                     scale * kLog2e);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nkb = (T + KV_BK - 1) / KV_BK;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<Pol, D>), dim3(nkb * B * Hkv), dim3(BWD_THREADS), 0, stream,
+                     (const in_t*)q, (const in_t*)k, (const in_t*)v, (const in_t*)rho,
+                     (const in_t*)d_o, lse, c_aux, G, dl, dk, dv, B, Hq, Hkv, T, scale,
+                     scale * kLog2e);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(int dtype, const void* q, const void* k, const void* v, const void* rho,
+                      const void* d_o, const float* o, const float* lse, const float* c_aux,
+                      const float* vbar_aux, float* dq, float* dk, float* dv, float* drho, int B,
+                      int Hq, int Hkv, int T, int d, float scale, float* ws, hipStream_t stream) {
+  if (dtype == PLX_BF16) {
+    if (d == 64)
+      return launch_bwd_t<PolBF16, 64>(q, k, v, rho, d_o, o, lse, c_aux, vbar_aux, dq, dk, dv, drho, B, Hq, Hkv, T, scale, ws, stream);
+    return launch_bwd_t<PolBF16, 128>(q, k, v, rho, d_o, o, lse, c_aux, vbar_aux, dq, dk, dv, drho, B, Hq, Hkv, T, scale, ws, stream);
+  }
+  if (d == 64)
+    return launch_bwd_t<PolF32, 64>(q, k, v, rho, d_o, o, lse, c_aux, vbar_aux, dq, dk, dv, drho, B, Hq, Hkv, T, scale, ws, stream);
+  return launch_bwd_t<PolF32, 128>(q, k, v, rho, d_o, o, lse, c_aux, vbar_aux, dq, dk, dv, drho, B, Hq, Hkv, T, scale, ws, stream);
+}
+
+}  // namespace plx

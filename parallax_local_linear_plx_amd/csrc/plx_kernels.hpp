@@ -1,0 +1,31 @@
+// Internal launch entry points of the kernel translation units.  Arguments are
+// validated by the C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "plx.h"
+
+namespace plx {
+
+hipError_t launch_fwd(int dtype, const void* q, const void* k, const void* v, const void* rho,
+                      float* o, float* lse, float* c_aux, float* vbar_aux, int B, int Hq, int Hkv,
+                      int T, int d, float scale, hipStream_t stream);
+
+// Decode: key-split partial kernel followed by the merge kernel.
+int decode_auto_splits(int B, int Hkv, int S_max);
+int decode_chunk_keys(int S_max, int num_splits);
+size_t decode_record_floats(int d);
+hipError_t launch_decode(int dtype, const void* q, const void* rho, const void* k_cache,
+                         const void* v_cache, const int32_t* ctx_len, float* o, float* lse, int B,
+                         int Hq, int Hkv, int S_max, int d, float scale, int num_splits,
+                         float* partials, hipStream_t stream);
+
+hipError_t launch_bwd(int dtype, const void* q, const void* k, const void* v, const void* rho,
+                      const void* d_o, const float* o, const float* lse, const float* c_aux,
+                      const float* vbar_aux, float* dq, float* dk, float* dv, float* drho, int B,
+                      int Hq, int Hkv, int T, int d, float scale, float* ws, hipStream_t stream);
+
+}  // namespace plx

@@ -188,15 +188,18 @@ def _projected_probe(seq_x, seq_w, B, Hq, T, d, x_dim, dtype) -> Tensor:
 
 
 def make_decode(B, Hq, Hkv, d, ctx, S_max=None, dtype="bf16", seed=0, rho_std=0.1,
-                ctx_range=None, scale=None, name="decode") -> Workload:
+                ctx_range=None, scale=None, name="decode", ctx_list=None) -> Workload:
     """One new query and probe per sequence against a [B, Hkv, S_max, d] KV cache.
 
     ``ctx`` is the uniform context length, or ignored when ``ctx_range=(lo, hi)``
-    is given: then ctx_len[b] ~ U{lo..hi}, both ends inclusive, drawn first.
+    is given: then ctx_len[b] ~ U{lo..hi}, both ends inclusive, drawn first;
+    ``ctx_list`` gives the lengths explicitly.
     Cache rows at or beyond ctx_len[b] hold bf16 NaN canaries.
     """
     r = _roles(seed)
-    if ctx_range is not None:
+    if ctx_list is not None:
+        ctx_len = np.asarray(ctx_list, dtype=np.int32)
+    elif ctx_range is not None:
         lo, hi = ctx_range
         ctx_len = np.random.default_rng(r["ctx_len"]).integers(lo, hi, size=B,
                                                                endpoint=True).astype(np.int32)

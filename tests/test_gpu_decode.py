@@ -1,0 +1,144 @@
+"""GPU parity of plx_decode (split-K partials + merge) against the fp64 oracle."""
+
+import numpy as np
+import pytest
+
+from oracle import plx_oracle as orc
+from parallax_local_linear_plx_amd import inputs
+from tests._util import LSE_ABS, check_bf16, check_fp32, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(wl):
+    import torch
+
+    t = {n: to_device(x) for n, x in wl.tensors.items()}
+    t["q"] = t["q"].reshape(wl.B, wl.Hq, wl.d)
+    t["rho"] = t["rho"].reshape(wl.B, wl.Hq, wl.d)
+    t["ctx"] = torch.from_numpy(wl.ctx_len.astype(np.int32)).cuda()
+    return t
+
+
+def _run(wl, num_splits=0, t=None):
+    import torch
+
+    from parallax_local_linear_plx_amd import plx_decode
+
+    if t is None:
+        t = _dev(wl)
+    o = torch.full((wl.B, wl.Hq, wl.d), float("nan"), dtype=torch.float32, device="cuda")
+    out = plx_decode(t["q"], t["rho"], t["k"], t["v"], t["ctx"], wl.scale, num_splits=num_splits, o=o)
+    torch.cuda.synchronize()
+    return {n: x.cpu().numpy() for n, x in out.items()}
+
+
+def _oracle(wl, heads=None):
+    q = wl.tensors["q"].f64().reshape(wl.B, wl.Hq, wl.d)
+    rho = wl.tensors["rho"].f64().reshape(wl.B, wl.Hq, wl.d)
+
+    def fetch(b, hk, n):
+        return (wl.tensors["k"].f64_slice((b, hk, slice(0, n))),
+                wl.tensors["v"].f64_slice((b, hk, slice(0, n))))
+
+    return orc.decode_forward(q, rho, fetch, wl.Hkv, wl.ctx_len, wl.scale, heads=heads)
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 3, 7])
+def test_bf16_ragged_small(gpu_lib, num_splits):
+    say(f"case decode bf16 B3 Hq4 Hkv2 S700 ragged splits={num_splits}")
+    wl = inputs.make_decode(3, 4, 2, 128, 0, S_max=700, dtype="bf16", seed=50, ctx_list=[700, 1, 333])
+    got = _run(wl, num_splits)
+    ref = _oracle(wl)
+    check_bf16(got["o"].reshape(-1, wl.d), ref["o"], "o")
+    assert np.max(np.abs(got["lse"].reshape(-1) - ref["lse"])) <= LSE_ABS
+
+
+@pytest.mark.parametrize("G,d", [(1, 64), (8, 128), (16, 64), (2, 128)])
+def test_fp32_group_sizes(gpu_lib, G, d):
+    say(f"case decode fp32 G{G} d{d}")
+    wl = inputs.make_decode(2, 2 * G, 2, d, 0, S_max=300, dtype="f32", seed=60 + G, ctx_range=(1, 300),
+                            rho_std=0.5)
+    got = _run(wl, 2)
+    ref = _oracle(wl)
+    check_fp32(got["o"].reshape(-1, d), ref["o"], "o")
+    check_fp32(got["lse"].reshape(-1), ref["lse"], "lse")
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 5, 64])
+def test_key_count_probe_is_exact(gpu_lib, num_splits):
+    """q = 0: exp(LSE) must round to ctx_len[b] exactly for every split count."""
+    ctx = np.array([5000, 1, 129, 4097], np.int32)
+    wl = inputs.make_decode(4, 4, 2, 128, 0, S_max=5000, dtype="bf16", seed=70, ctx_list=ctx)
+    wl.tensors["q"].data[...] = 0
+    got = _run(wl, num_splits)
+    n = np.rint(np.exp(got["lse"].astype(np.float64))).astype(np.int64)
+    assert np.array_equal(n, np.repeat(ctx[:, None], wl.Hq, axis=1))
+
+
+def test_mapping_probe_and_invalid_lengths(gpu_lib):
+    """V constant per (b, kv head): o rounds to that code; ctx_len outside
+    [1, S_max] gives NaN for that sequence only."""
+    import torch
+
+    B, Hq, Hkv, S, d = 4, 8, 2, 600, 128
+    wl = inputs.make_decode(B, Hq, Hkv, d, S, dtype="bf16", seed=80)
+    codes = (np.arange(B * Hkv).reshape(B, Hkv) + 1).astype(np.float32)
+    v = np.broadcast_to(codes[:, :, None, None], (B, Hkv, S, d)).astype(np.float32)
+    wl.tensors["v"].data[...] = inputs.bf16_round_bits(v)
+    t = _dev(wl)
+    ctx = np.array([600, 0, 601, 17], np.int32)
+    t["ctx"] = torch.from_numpy(ctx).cuda()
+    got = _run(wl, 0, t)
+    o = got["o"]
+    want = np.repeat(codes, Hq // Hkv, axis=1)
+    for b in (0, 3):
+        assert np.array_equal(np.rint(o[b]), np.broadcast_to(want[b][:, None], o[b].shape))
+    for b in (1, 2):
+        assert np.all(np.isnan(o[b])) and np.all(np.isnan(got["lse"][b]))
+
+
+def test_decode_matches_prefill_last_row(gpu_lib):
+    """Decode over the first t cache rows equals the prefill output at row t-1
+    (both on the GPU, both checked against the oracle)."""
+    import torch
+
+    from parallax_local_linear_plx_amd import plx_decode, plx_fwd_prefill
+
+    B, Hq, Hkv, T, d = 2, 4, 2, 257, 128
+    wl = inputs.make_prefill(B, Hq, Hkv, T, d, dtype="bf16", seed=90)
+    t = {n: to_device(x) for n, x in wl.tensors.items()}
+    pre = plx_fwd_prefill(t["q"], t["k"], t["v"], t["rho"], wl.scale)
+    ctx = torch.tensor([T, 100], dtype=torch.int32, device="cuda")
+    qd = torch.stack([t["q"][0, :, T - 1], t["q"][1, :, 99]]).contiguous()
+    rd = torch.stack([t["rho"][0, :, T - 1], t["rho"][1, :, 99]]).contiguous()
+    dec = plx_decode(qd, rd, t["k"], t["v"], ctx, wl.scale, num_splits=2)
+    torch.cuda.synchronize()
+    o_pre = torch.stack([pre["o"][0, :, T - 1], pre["o"][1, :, 99]]).cpu().numpy()
+    assert np.max(np.abs(dec["o"].cpu().numpy() - o_pre)) < 5e-3
+
+
+def test_bf16_decode_full_size_sampled_heads(gpu_lib):
+    """Batched decode at full size: B=64, Hq=16, Hkv=8, ctx=8192, d=128."""
+    say("case decode bf16 B64 Hq16 Hkv8 ctx8192 d128 (sampled heads)")
+    wl = inputs.bf16_decode()
+    got = _run(wl)
+    assert np.all(np.isfinite(got["o"]))
+    g = np.random.default_rng(7)
+    heads = [(0, 0), (63, 15), (31, 8)] + [(int(g.integers(64)), int(g.integers(16))) for _ in range(21)]
+    ref = _oracle(wl, heads)
+    check_bf16(np.array([got["o"][b, h] for b, h in heads]), ref["o"], "o (sampled heads)")
+    assert np.max(np.abs(np.array([got["lse"][b, h] for b, h in heads]) - ref["lse"])) <= LSE_ABS
+
+
+def test_bf16_long_decode_full_size_sampled_heads(gpu_lib):
+    """Long-context ragged decode at full size: B=8, ctx ~ U{16384..131072}."""
+    say("case long decode bf16 B8 Hq16 Hkv8 ctx 16384-131072 d128 (sampled heads)")
+    wl = inputs.bf16_long_decode()
+    say(f"  ctx_len = {wl.ctx_len.tolist()}")
+    got = _run(wl)
+    assert np.all(np.isfinite(got["o"]))
+    heads = [(b, (5 * b) % 16) for b in range(8)] + [(int(np.argmax(wl.ctx_len)), 15)]
+    ref = _oracle(wl, heads)
+    check_bf16(np.array([got["o"][b, h] for b, h in heads]), ref["o"], "o (sampled heads)")
+    assert np.max(np.abs(np.array([got["lse"][b, h] for b, h in heads]) - ref["lse"])) <= LSE_ABS
