@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the Parallax operator on one MI355X.
+
+Headline (``value``): causal GQA prefill in bf16 with fp32 accumulation,
+B=4, Hq=16, Hkv=8, T=4096, d=128, rho = W_R x, in TFLOP/s over the method's
+four causal GEMM-equivalents (QK, rho K, PV, (P.R)V: 2*d flops per (i, j<=i)
+pair each).  The same JSON line also carries the decode workloads (batched
+B=64 ctx=8192, and long-context ragged B=8 ctx ~ U{16384..131072}) in
+microseconds per step and HBM GB/s, and the training step (forward + backward,
+B=8 T=4096) in TFLOP/s per pass.
+
+Timing: HIP events recorded on the stream the kernels run on (torch's current
+stream), W warm-up steps, then exactly K timed steps between two device
+synchronisations.  The CPU baseline is the fp64 oracle on a bounded sample of
+prefill rows, timed on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|decode|train|all]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill TFLOP/s & %MFMA peak; decode µs/step & HBM GB/s vs peak"
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 / fp16 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_steps(fn, steps, warmup):
+    """Average ms per call of fn over `steps` timed calls (after `warmup`)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def causal_pairs(T):
+    return T * (T + 1) // 2
+
+
+# ------------------------------------------------------------------ prefill
+def bench_prefill(steps, warmup):
+    import torch
+
+    from parallax_local_linear_plx_amd import inputs, plx_fwd_prefill
+
+    B, Hq, Hkv, T, d = 4, 16, 8, 4096, 128
+    q = inputs.device_normal((B, Hq, T, d), 1.0, 21)
+    k = inputs.device_normal((B, Hkv, T, d), 1.0, 22)
+    v = inputs.device_normal((B, Hkv, T, d), 1.0, 23)
+    rho = inputs.device_projected_probe(B, Hq, T, d, 24)
+    o = torch.empty((B, Hq, T, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+
+    def step():
+        plx_fwd_prefill(q, k, v, rho, o=o, lse=True)
+
+    ms = time_steps(step, steps, warmup)
+    flops = 4 * 2 * d * causal_pairs(T) * B * Hq
+    tflops = flops / (ms * 1e-3) / 1e12
+    # bytes the kernel must move at least once: q, rho, k, v in; o, lse out
+    algo_bytes = (2 * B * Hq * T * d + 2 * B * Hkv * T * d) * 2 + B * Hq * T * (d + 1) * 4
+    cfg = {"workload": f"bf16 causal GQA prefill B={B} Hq={Hq} Hkv={Hkv} T={T} d={d}, rho=W_R x",
+           "B": B, "Hq": Hq, "Hkv": Hkv, "T": T, "d": d}
+    return {"ms": ms, "tflops": tflops, "flops": flops, "bytes": algo_bytes, "config": cfg}
+
+
+# ------------------------------------------------------------------- decode
+def bench_decode(steps, warmup, B, ctx_len, S_max, name, seed):
+    import torch
+
+    from parallax_local_linear_plx_amd import inputs, plx_decode
+
+    Hq, Hkv, d = 16, 8, 128
+    kc = inputs.device_normal((B, Hkv, S_max, d), 1.0, seed)
+    vc = inputs.device_normal((B, Hkv, S_max, d), 1.0, seed + 1)
+    q = inputs.device_normal((B, Hq, d), 1.0, seed + 2)
+    rho = inputs.device_normal((B, Hq, d), 0.1, seed + 3)
+    ctx = torch.from_numpy(np.asarray(ctx_len, np.int32)).cuda()
+    o = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    from parallax_local_linear_plx_amd import decode_workspace_size
+
+    ws = torch.empty(decode_workspace_size(B, Hq, Hkv, S_max, d, 0), dtype=torch.uint8, device="cuda")
+
+    def step():
+        plx_decode(q, rho, kc, vc, ctx, num_splits=0, workspace=ws, o=o, lse=False)
+
+    ms = time_steps(step, steps, warmup)
+    kv_bytes = int(np.sum(ctx_len)) * Hkv * d * 2 * 2
+    io_bytes = B * Hq * d * (2 + 2 + 4)
+    gbs = (kv_bytes + io_bytes) / (ms * 1e-3) / 1e9
+    flops = int(np.sum(ctx_len)) * Hq * d * 8
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"workload": name, "us_per_step": ms * 1e3, "us_per_token": ms * 1e3,
+            "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS, "bytes": kv_bytes + io_bytes,
+            "flop_per_byte": flops / (kv_bytes + io_bytes),
+            "ctx_len_sum": int(np.sum(ctx_len))}
+
+
+# ------------------------------------------------------------------ training
+def bench_train(steps, warmup):
+    import torch
+
+    from parallax_local_linear_plx_amd import bwd_workspace_size, inputs, plx_bwd, plx_fwd_prefill
+
+    B, Hq, Hkv, T, d = 8, 16, 8, 4096, 128
+    q = inputs.device_normal((B, Hq, T, d), 1.0, 51)
+    k = inputs.device_normal((B, Hkv, T, d), 1.0, 52)
+    v = inputs.device_normal((B, Hkv, T, d), 1.0, 53)
+    rho = inputs.device_normal((B, Hq, T, d), 0.1, 54)
+    d_o = inputs.device_normal((B, Hq, T, d), 1.0, 55)
+    fwd = plx_fwd_prefill(q, k, v, rho, aux=True)
+    ws = torch.empty(bwd_workspace_size(B, Hq, Hkv, T, d), dtype=torch.uint8, device="cuda")
+    grads = {
+        "dq": torch.empty_like(fwd["o"]), "drho": torch.empty_like(fwd["o"]),
+        "dk": torch.empty((B, Hkv, T, d), dtype=torch.float32, device="cuda"),
+        "dv": torch.empty((B, Hkv, T, d), dtype=torch.float32, device="cuda"),
+    }
+
+    def fstep():
+        plx_fwd_prefill(q, k, v, rho, o=fwd["o"], aux=True)
+
+    def bstep():
+        plx_bwd(q, k, v, rho, d_o, fwd["o"], fwd["lse"], fwd["c"], fwd["vbar"], workspace=ws, grads=grads)
+
+    ms_f = time_steps(fstep, steps, warmup)
+    ms_b = time_steps(bstep, steps, warmup)
+    fl_f = 4 * 2 * d * causal_pairs(T) * B * Hq
+    fl_b = 8 * 2 * d * causal_pairs(T) * B * Hq
+    out = {"workload": f"bf16 training step fwd+bwd B={B} Hq={Hq} Hkv={Hkv} T={T} d={d}",
+           "fwd_ms": ms_f, "bwd_ms": ms_b, "step_ms": ms_f + ms_b,
+           "fwd_tflops": fl_f / (ms_f * 1e-3) / 1e12, "bwd_tflops": fl_b / (ms_b * 1e-3) / 1e12,
+           "step_tflops": (fl_f + fl_b) / ((ms_f + ms_b) * 1e-3) / 1e12}
+    out["bwd_mfma_frac"] = out["bwd_tflops"] / PEAK_BF16_TFLOPS
+    del q, k, v, rho, d_o, fwd, grads
+    torch.cuda.empty_cache()
+    return out
+
+
+# ------------------------------------------------------------- CPU baseline
+def cpu_baseline(budget_s=12.0):
+    """The fp64 oracle on sampled rows of the prefill workload, on host cores.
+    Rate in the headline's unit (TFLOP/s over the four GEMM-equivalents)."""
+    from oracle import plx_oracle as orc
+    from parallax_local_linear_plx_amd import inputs
+
+    T, d = 4096, 128
+    wl = inputs.make_prefill(1, 2, 1, T, d, dtype="bf16", seed=2, rho_projected=True)
+    ten = wl.tensors
+    g = np.random.default_rng(0)
+    flops = 0
+    n_rows = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s or n_rows < 8:
+        h = int(g.integers(2))
+        i = int(g.integers(T))
+        orc.row_forward(ten["q"].f64_slice((0, h, i)), ten["k"].f64_slice((0, 0, slice(0, i + 1))),
+                        ten["v"].f64_slice((0, 0, slice(0, i + 1))), ten["rho"].f64_slice((0, h, i)),
+                        wl.scale)
+        flops += 4 * 2 * d * (i + 1)
+        n_rows += 1
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_rows} random rows (uniform i in [0,4096)) of the B=4 Hq=16 T=4096 d=128 "
+                      f"prefill, fp64 numpy with explicit covariance per row, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "train"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the operator shards by (batch, kv head) with no exchange, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from parallax_local_linear_plx_amd import binding
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.lib()  # fail loudly if the HIP library is missing
+
+    res = {}
+    if args.only in ("all", "prefill"):
+        log("prefill ...")
+        res["prefill"] = bench_prefill(args.steps, args.warmup)
+        log(f"  {res['prefill']['ms'] * 1e3:.1f} us  {res['prefill']['tflops']:.1f} TFLOP/s")
+    if args.only in ("all", "decode"):
+        log("decode B64 ctx8192 ...")
+        res["decode"] = bench_decode(args.steps, args.warmup, 64, [8192] * 64, 8192,
+                                     "bf16 decode B=64 Hq=16 Hkv=8 ctx=8192 d=128", 31)
+        log(f"  {res['decode']['us_per_step']:.1f} us  {res['decode']['GB/s']:.0f} GB/s")
+        from parallax_local_linear_plx_amd import inputs
+
+        ctx = inputs.long_decode_ctx()
+        log(f"long decode B8 ctx {ctx.tolist()} ...")
+        res["decode_long"] = bench_decode(args.steps, args.warmup, 8, ctx, 131072,
+                                          "bf16 long-context decode B=8 Hq=16 Hkv=8 "
+                                          "ctx~U{16384..131072} d=128, split-K", 41)
+        log(f"  {res['decode_long']['us_per_step']:.1f} us  {res['decode_long']['GB/s']:.0f} GB/s")
+    if args.only in ("all", "train"):
+        log("training step ...")
+        res["train"] = bench_train(max(3, args.steps // 4), max(1, args.warmup // 2))
+        log(f"  fwd {res['train']['fwd_ms']:.2f} ms  bwd {res['train']['bwd_ms']:.2f} ms")
+
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded device draws, q,k,v~N(0,1), rho=W_R x / N(0,0.1^2))"}
+    if "prefill" in res:
+        p = res["prefill"]
+        line.update({"value": round(p["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(p["ms"], 4),
+                     "config": p["config"],
+                     "roofline": {"bound": "mfma", "achieved": round(p["tflops"], 2),
+                                  "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                  "kernel": "fwd_kernel<PolBF16,128>",
+                                  "algorithmic_flops_per_launch": p["flops"]}})
+    else:
+        line.update({"value": None, "unit": "TFLOP/s", "ms_per_step": None, "config": {"workload": args.only}})
+    for key in ("decode", "decode_long", "train"):
+        if key in res:
+            line[key] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res[key].items()}
+    if not args.no_cpu and args.only in ("all", "prefill"):
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -212,24 +212,31 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq_kernel(
 
 // --------------------------------------------------------------- dK and dV
 constexpr int KV_BK = 128;  // keys per workgroup (32 per wave)
-constexpr int KV_BQ = 64;   // queries per LDS tile
+
+// Queries per LDS tile: 64 for 2-byte inputs; 32 for fp32 so that the six
+// staged tiles of d = 128 stay within the 160 KB of LDS.
+template <class Pol>
+constexpr int kv_bq() {
+  return sizeof(typename Pol::in_t) == 2 ? 64 : 32;
+}
 
 template <class Pol, int D>
 struct DkvSmem {
   using in_t = typename Pol::in_t;
   using vel_t = typename Pol::vel_t;
+  static constexpr int BQ = kv_bq<Pol>();
   static constexpr int LD = D + 16 / sizeof(in_t);
-  static constexpr int TLD = KV_BQ + 4;
-  in_t q[KV_BQ * LD];
-  in_t r[KV_BQ * LD];
-  in_t g[KV_BQ * LD];
-  vel_t qt[D * TLD];
-  vel_t rt[D * TLD];
-  vel_t gt[D * TLD];
-  float lse2[KV_BQ];
-  float c[KV_BQ];
-  float G[KV_BQ];
-  float dl[KV_BQ];
+  static constexpr int TLD = BQ + 4;
+  alignas(16) in_t q[BQ * LD];
+  alignas(16) in_t r[BQ * LD];
+  alignas(16) in_t g[BQ * LD];
+  alignas(16) vel_t qt[D * TLD];
+  alignas(16) vel_t rt[D * TLD];
+  alignas(16) vel_t gt[D * TLD];
+  alignas(16) float lse2[BQ];
+  alignas(16) float c[BQ];
+  alignas(16) float G[BQ];
+  alignas(16) float dl[BQ];
 };
 
 template <class Pol, int D>
@@ -246,6 +253,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv_kernel(
   constexpr int KW = Pol::KW, KSTEP = Pol::KSTEP;
   constexpr int NS = D / KSTEP, NV = 32 / KSTEP, ND = D / 32;
   using SM = DkvSmem<Pol, D>;
+  constexpr int KV_BQ = SM::BQ;
   __shared__ SM sm;
 
   const int bhk_count = B * Hkv;

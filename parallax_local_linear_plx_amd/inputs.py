@@ -251,3 +251,36 @@ def bf16_training(seed=5, B=8, Hq=16, Hkv=8, T=4096, d=128):
     """Training step: causal forward + backward with upstream dO ~ N(0, 1)."""
     return make_prefill(B, Hq, Hkv, T, d, dtype="bf16", seed=seed, with_grad=True,
                         name=f"bf16_train_B{B}_Hq{Hq}_Hkv{Hkv}_T{T}_d{d}")
+
+
+# ---------------------------------------------------------------------------
+# Device-side draws for timing runs (same shapes and distributions, seeded
+# torch generators on the GPU, so multi-GB caches need no host round trip).
+# ---------------------------------------------------------------------------
+
+def device_normal(shape, std, seed, device="cuda", dtype="bf16"):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(torch.bfloat16) if dtype == "bf16" else x
+
+
+def device_projected_probe(B, Hq, T, d, seed, x_dim=1024, device="cuda"):
+    """rho = W_R x on the device: x ~ N(0,1)^x_dim per token, W_R ~ N(0, 1/x_dim) per head."""
+    import torch
+
+    x = device_normal((B, T, x_dim), 1.0, seed, device, "f32")
+    w = device_normal((Hq, d, x_dim), 1.0 / np.sqrt(x_dim), seed + 1, device, "f32")
+    wt = w.transpose(1, 2).contiguous()  # [Hq, x_dim, d], fp32
+    rho = torch.matmul(x[:, None], wt[None])  # [B, Hq, T, d]
+    return rho.to(torch.bfloat16).contiguous()
+
+
+def long_decode_ctx(seed=4, B=8, lo=16384, hi=131072):
+    """The ragged context lengths of the long-context decode workload (drawn first)."""
+    r = _roles(seed)
+    return np.random.default_rng(r["ctx_len"]).integers(lo, hi, size=B, endpoint=True).astype(np.int32)

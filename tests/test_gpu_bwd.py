@@ -1,0 +1,140 @@
+"""GPU parity of plx_bwd (dQ, dK, dV, drho) against the fp64 oracle."""
+
+import numpy as np
+import pytest
+
+from oracle import plx_oracle as orc
+from parallax_local_linear_plx_amd import inputs
+from tests._util import check_bf16, check_fp32, grad_floor, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(wl):
+    import torch
+
+    from parallax_local_linear_plx_amd import plx_bwd, plx_fwd_prefill
+
+    t = {n: to_device(x) for n, x in wl.tensors.items()}
+    fwd = plx_fwd_prefill(t["q"], t["k"], t["v"], t["rho"], wl.scale, aux=True)
+    nan = float("nan")
+    grads = {
+        "dq": torch.full(t["q"].shape, nan, dtype=torch.float32, device="cuda"),
+        "dk": torch.full(t["k"].shape, nan, dtype=torch.float32, device="cuda"),
+        "dv": torch.full(t["v"].shape, nan, dtype=torch.float32, device="cuda"),
+        "drho": torch.full(t["rho"].shape, nan, dtype=torch.float32, device="cuda"),
+    }
+    plx_bwd(t["q"], t["k"], t["v"], t["rho"], t["d_o"], fwd["o"], fwd["lse"], fwd["c"], fwd["vbar"],
+            wl.scale, grads=grads)
+    torch.cuda.synchronize()
+    return {n: x.cpu().numpy() for n, x in grads.items()}
+
+
+def _oracle(wl):
+    f = {n: x.f64() for n, x in wl.tensors.items()}
+    return orc.prefill_backward(f["q"], f["k"], f["v"], f["rho"], f["d_o"], wl.scale)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,d", [(1, 1, 1, 128, 64), (2, 4, 2, 150, 128), (1, 2, 1, 1, 64),
+                                          (1, 3, 1, 97, 64)])
+def test_fp32_gradients(gpu_lib, B, Hq, Hkv, T, d):
+    say(f"case bwd fp32 B{B} Hq{Hq} Hkv{Hkv} T{T} d{d}")
+    wl = inputs.make_prefill(B, Hq, Hkv, T, d, dtype="f32", seed=100 + T, rho_std=0.1, with_grad=True)
+    got = _run(wl)
+    ref = _oracle(wl)
+    for n in ("dq", "dk", "dv", "drho"):
+        check_fp32(got[n], ref[n], n, floor=grad_floor(ref[n]))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,d", [(1, 4, 2, 300, 128), (1, 2, 2, 129, 64), (2, 2, 1, 77, 128)])
+def test_bf16_gradients(gpu_lib, B, Hq, Hkv, T, d):
+    """Training-workload probe scale, rho ~ N(0, 0.1^2): the bf16 bars."""
+    say(f"case bwd bf16 B{B} Hq{Hq} Hkv{Hkv} T{T} d{d}")
+    wl = inputs.make_prefill(B, Hq, Hkv, T, d, dtype="bf16", seed=200 + T, with_grad=True)
+    got = _run(wl)
+    ref = _oracle(wl)
+    for n in ("dq", "dk", "dv", "drho"):
+        check_bf16(got[n], ref[n], n)
+
+
+def test_bf16_gradients_projected_probe_scale(gpu_lib):
+    """Informational: the prefill workload's probe rho = W_R x (~N(0,1) per
+    component, ten times the training scale).  The fp16 operand P(1 + c - r)
+    of dV then carries |r| up to ~40, so dV's max-abs error reaches ~2.5e-2;
+    the mean-abs bar still holds and max-abs is held to 5e-2."""
+    say("case bwd bf16 B1 Hq2 Hkv1 T200 d128 projected rho")
+    wl = inputs.make_prefill(1, 2, 1, 200, 128, dtype="bf16", seed=400, rho_projected=True,
+                             with_grad=True)
+    got = _run(wl)
+    ref = _oracle(wl)
+    for n in ("dq", "dk", "dv", "drho"):
+        check_bf16(got[n], ref[n], n, max_abs=5e-2)
+
+
+def test_zero_probe_gradients_are_attention_gradients(gpu_lib):
+    """rho = 0: dQ, dK, dV equal torch autograd of causal SDPA (fp64, CPU)."""
+    import torch
+
+    B, Hq, Hkv, T, d = 1, 2, 1, 70, 64
+    wl = inputs.make_prefill(B, Hq, Hkv, T, d, dtype="f32", seed=300, with_grad=True)
+    wl.tensors["rho"].data[...] = 0
+    got = _run(wl)
+    f = {n: torch.tensor(x.f64(), requires_grad=n in ("q", "k", "v")) for n, x in wl.tensors.items()}
+    out = torch.nn.functional.scaled_dot_product_attention(
+        f["q"], f["k"].repeat_interleave(Hq // Hkv, 1), f["v"].repeat_interleave(Hq // Hkv, 1),
+        is_causal=True, scale=wl.scale)
+    out.backward(f["d_o"])
+    for n, ref in (("dq", f["q"].grad.numpy()), ("dk", f["k"].grad.numpy()), ("dv", f["v"].grad.numpy())):
+        check_fp32(got[n], ref, n, floor=grad_floor(ref))
+
+
+def test_repeat_runs_are_bitwise_identical(gpu_lib):
+    wl = inputs.make_prefill(1, 2, 1, 260, 128, dtype="bf16", seed=301, with_grad=True)
+    a = _run(wl)
+    b = _run(wl)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_bf16_training_full_size(gpu_lib):
+    """Training step at full size (B=8, Hq=16, Hkv=8, T=4096, d=128): sampled
+    rows of dQ / drho and the last keys of dK / dV against the oracle, plus two
+    invariants over every key: shifting all keys by one vector leaves o
+    unchanged (sum_j dK_j = 0), shifting all values by u shifts o by u
+    (sum_j dV_j = sum over the group's rows of dO)."""
+    say("case bwd bf16 B8 Hq16 Hkv8 T4096 d128 (sampled)")
+    wl = inputs.bf16_training()
+    got = _run(wl)
+    for n in got:
+        assert np.all(np.isfinite(got[n])), n
+    T, Hq, Hkv = wl.T, wl.Hq, wl.Hkv
+    ten = wl.tensors
+
+    def row(b, h, hk, i):
+        return (ten["q"].f64_slice((b, h, i)), ten["k"].f64_slice((b, hk, slice(0, i + 1))),
+                ten["v"].f64_slice((b, hk, slice(0, i + 1))), ten["rho"].f64_slice((b, h, i)),
+                ten["d_o"].f64_slice((b, h, i)))
+
+    g = np.random.default_rng(5)
+    rows = [(0, 0, 0), (7, 15, 4095), (3, 4, 2000)] + [
+        (int(g.integers(8)), int(g.integers(16)), int(g.integers(4096))) for _ in range(13)]
+    rdq, rdr = [], []
+    for b, h, i in rows:
+        qi, K, V, ri, gi = row(b, h, h // (Hq // Hkv), i)
+        dq, _, _, dr = orc.row_backward(qi, K, V, ri, gi, wl.scale)
+        rdq.append(dq)
+        rdr.append(dr)
+    check_bf16(np.array([got["dq"][b, h, i] for b, h, i in rows]), np.array(rdq), "dq (sampled rows)")
+    check_bf16(np.array([got["drho"][b, h, i] for b, h, i in rows]), np.array(rdr), "drho (sampled rows)")
+    keys = [(0, 0, T - 1), (5, 7, T - 2), (7, 3, T - 9)]
+    dk, dv = orc.prefill_backward_kv_rows(row, keys, T, Hq, Hkv, wl.scale)
+    check_bf16(np.array([got["dk"][b, hk, j] for b, hk, j in keys]), dk, "dk (last keys)")
+    check_bf16(np.array([got["dv"][b, hk, j] for b, hk, j in keys]), dv, "dv (last keys)")
+    # invariants over all keys
+    sum_dk = got["dk"].astype(np.float64).sum(axis=2)
+    scale_dk = np.abs(got["dk"]).astype(np.float64).sum(axis=2)
+    assert np.all(np.abs(sum_dk) <= 2e-3 * scale_dk + 1e-2), float(np.max(np.abs(sum_dk)))
+    sum_dv = got["dv"].astype(np.float64).sum(axis=2)
+    d_o = ten["d_o"].f64().reshape(wl.B, Hkv, Hq // Hkv, T, wl.d).sum(axis=(2, 3))
+    scale_dv = np.abs(got["dv"]).astype(np.float64).sum(axis=2)
+    assert np.all(np.abs(sum_dv - d_o) <= 2e-3 * scale_dv + 1e-2), float(np.max(np.abs(sum_dv - d_o)))
