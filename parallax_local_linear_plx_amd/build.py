@@ -25,12 +25,17 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
+# Device-side code generation: MFMA accumulators in the VGPR form.  The kernels
+# rescale and read their accumulators on the VALU; with the AGPR form the
+# register allocator shuttles every accumulator between the two files on each
+# loop iteration (hundreds of v_accvgpr moves per 64-key tile).
+DEVICE = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src: str, resource_usage: bool) -> tuple[str, str]:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *COMMON, "-c", path, "-o", obj]
+    cmd = [HIPCC, *COMMON, *DEVICE, "-c", path, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, *COMMON, "-x", "hip", "-c", path, "-o", obj]
     if resource_usage and src.endswith(".hip"):

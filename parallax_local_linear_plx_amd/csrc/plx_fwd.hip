@@ -17,10 +17,18 @@
 // [Q; rho] K^T is two MFMA chains sharing every K operand.
 //
 // Work split: a workgroup (4 waves) owns 128 query rows of one (b, h);
-// each wave owns 32 rows.  Keys stream in tiles of 64 through LDS:
-//   K tile   row-major  [64][D + pad]   (A operand of S^T = K Q^T, R^T = K rho^T)
-//   V tile   transposed [D][64 + pad]   (A operand of O^T = V^T P^T, U^T = V^T (P.R)^T)
-// Q and rho stay in registers as B operands for the whole pass.
+// each wave owns 32 rows, with its Q and rho rows held as MFMA B operands
+// for the whole pass.  Keys stream in tiles of 64 through double-buffered LDS:
+//   K tile  row-major [64][D + pad]   A operand of S^T = K Q^T and R^T = K rho^T
+//   V tile  bf16 path: row-major fp16 [64][D + 32], read transposed by
+//           ds_read_b64_tr_b16 as the A operand of O^T = V^T P^T, U^T = V^T (P.R)^T;
+//           fp32 path: stored transposed [D][64 + 4].
+// Pipeline per 64-key iteration j (one barrier): global loads of K(j+2) and
+// V(j+1) are issued first into registers; for each 32-key sub-tile t the score
+// MFMAs of t+1 are issued before the softmax (VALU) and value MFMAs of t, so
+// the two overlap; last, the prefetched registers go to the free LDS buffers.
+// (The fp32 path, whose Q and rho operands alone take 128 registers at
+// d = 128, computes each sub-tile's scores just before its softmax.)
 #include "plx_common.hpp"
 #include "plx_kernels.hpp"
 
@@ -31,65 +39,353 @@ namespace {
 constexpr int FWD_BR = 128;
 constexpr int FWD_BC = 64;
 constexpr int FWD_THREADS = 256;
+// Lazy-rescale threshold (log2 units): p stays <= 16, so the fp16 operand
+// p * r overflows only for |r| = |rho . k| > 4094.
+constexpr float kRescaleLog2 = 4.f;
+
+template <class Pol>
+constexpr bool v_rowmajor() {
+  return sizeof(typename Pol::in_t) == 2;  // bf16 inputs: transpose-read path
+}
 
 template <class Pol, int D>
 struct FwdSmem {
   using in_t = typename Pol::in_t;
   using vel_t = typename Pol::vel_t;
-  static constexpr int KPAD = 16 / sizeof(in_t);
-  static constexpr int KLD = D + KPAD;       // K row stride (elements)
-  static constexpr int VLD = FWD_BC + 4;     // V^T row stride (elements)
-  in_t k[FWD_BC * KLD];
-  vel_t vt[D * VLD];
+  static constexpr int KLD = D + 16 / sizeof(in_t);  // K row stride (elements)
+  // V row stride: row-major fp16 rows offset by 64 bytes mod 256 so that the
+  // four rows one transpose read touches fall in distinct bank groups;
+  // transposed fp32 rows padded by 4.
+  static constexpr int VLD = v_rowmajor<Pol>() ? D + 32 : FWD_BC + 4;
+  static constexpr int VSIZE = v_rowmajor<Pol>() ? FWD_BC * VLD : D * VLD;
+  alignas(16) in_t k[2][FWD_BC * KLD];
+  alignas(16) vel_t v[2][VSIZE];
 };
 
-// Cooperative global -> LDS staging of one 64-key tile.  K is copied as is;
-// V is converted to the value-operand type and written transposed.  Rows at
-// or beyond T read as zero.
+// Per-thread prefetch registers for one K tile and one V tile.
 template <class Pol, int D>
-__device__ __forceinline__ void stage_kv_tile(FwdSmem<Pol, D>& sm, const typename Pol::in_t* kb,
-                                              const typename Pol::in_t* vb, int key0, int T) {
-  using in_t = typename Pol::in_t;
-  constexpr int CW = Pol::CW;
-  constexpr int CPR = D / CW;  // 16-byte chunks per row
-  const int tid = threadIdx.x;
-  // K: one chunk per item
-  for (int it = tid; it < FWD_BC * CPR; it += FWD_THREADS) {
-    const int r = it / CPR, c = (it % CPR) * CW;
-    const int key = key0 + r;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (key < T) val = *reinterpret_cast<const u32x4*>(kb + (size_t)key * D + c);
-    *reinterpret_cast<u32x4*>(&sm.k[r * FwdSmem<Pol, D>::KLD + c]) = val;
-  }
-  // V: two rows x one chunk per item, written as key pairs of the transpose
-  for (int it = tid; it < (FWD_BC / 2) * CPR; it += FWD_THREADS) {
-    const int rp = it / CPR, c = (it % CPR) * CW;
-    const int key = key0 + 2 * rp;
-    in_t a[CW], b[CW];
-    u32x4 va = {0u, 0u, 0u, 0u}, vb2 = {0u, 0u, 0u, 0u};
-    if (key < T) va = *reinterpret_cast<const u32x4*>(vb + (size_t)key * D + c);
-    if (key + 1 < T) vb2 = *reinterpret_cast<const u32x4*>(vb + (size_t)(key + 1) * D + c);
-    __builtin_memcpy(a, &va, 16);
-    __builtin_memcpy(b, &vb2, 16);
+struct TileRegs {
+  static constexpr int CPR = D / Pol::CW;                  // 16-byte chunks per row
+  static constexpr int N = FWD_BC * CPR / FWD_THREADS;     // chunks per thread per tile
+  u32x4 k[N];
+  u32x4 v[N];
+};
+
+template <class Pol, int D>
+__device__ __forceinline__ void gload_k(TileRegs<Pol, D>& r, const typename Pol::in_t* kb, int key0,
+                                        int T) {
+  constexpr int CPR = TileRegs<Pol, D>::CPR;
 #pragma unroll
-    for (int e = 0; e < CW; ++e) {
-      typename Pol::vel_t* dst = &sm.vt[(c + e) * FwdSmem<Pol, D>::VLD + 2 * rp];
-      dst[0] = Pol::to_vel(a[e]);
-      dst[1] = Pol::to_vel(b[e]);
+  for (int i = 0; i < TileRegs<Pol, D>::N; ++i) {
+    const int it = threadIdx.x + FWD_THREADS * i;
+    const int row = it / CPR, c = (it % CPR) * Pol::CW;
+    const int key = key0 + row;
+    // clamped in-bounds load, zeroed past T (no divergent branch)
+    const u32x4 val = *reinterpret_cast<const u32x4*>(kb + (size_t)min(key, T - 1) * D + c);
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    r.k[i] = key < T ? val : z;
+  }
+}
+
+// V: row-major chunks for the transpose-read path; pairs of rows (same
+// chunk) for the transposed fp32 layout.
+template <class Pol, int D>
+__device__ __forceinline__ void gload_v(TileRegs<Pol, D>& r, const typename Pol::in_t* vb, int key0,
+                                        int T) {
+  constexpr int CPR = TileRegs<Pol, D>::CPR;
+  if constexpr (v_rowmajor<Pol>()) {
+#pragma unroll
+    for (int i = 0; i < TileRegs<Pol, D>::N; ++i) {
+      const int it = threadIdx.x + FWD_THREADS * i;
+      const int row = it / CPR, c = (it % CPR) * Pol::CW;
+      const int key = key0 + row;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(vb + (size_t)min(key, T - 1) * D + c);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      r.v[i] = key < T ? val : z;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TileRegs<Pol, D>::N / 2; ++i) {
+      const int it = threadIdx.x + FWD_THREADS * i;
+      const int rp = it / CPR, c = (it % CPR) * Pol::CW;
+      const int key = key0 + 2 * rp;
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (key < T) a = *reinterpret_cast<const u32x4*>(vb + (size_t)key * D + c);
+      if (key + 1 < T) b = *reinterpret_cast<const u32x4*>(vb + (size_t)(key + 1) * D + c);
+      r.v[2 * i] = a;
+      r.v[2 * i + 1] = b;
     }
   }
 }
 
-// Value-operand (A of O^T = V^T P^T) for d-row `drow`, key sub-tile `st`,
-// MFMA step `s`, lane half `h`.
 template <class Pol, int D>
-__device__ __forceinline__ typename Pol::vop_t load_vt_op(const FwdSmem<Pol, D>& sm, int drow, int st,
-                                                          int s, int h) {
-  typename Pol::vop_t a;
-  const typename Pol::vel_t* row = &sm.vt[drow * FwdSmem<Pol, D>::VLD + 32 * st];
+__device__ __forceinline__ void lds_put_k(FwdSmem<Pol, D>& sm, int buf, const TileRegs<Pol, D>& r) {
+  constexpr int CPR = TileRegs<Pol, D>::CPR;
 #pragma unroll
-  for (int e = 0; e < Pol::KW; ++e) set_elem(a, e, row[acc_row(Pol::KW * s + e, h)]);
-  return a;
+  for (int i = 0; i < TileRegs<Pol, D>::N; ++i) {
+    const int it = threadIdx.x + FWD_THREADS * i;
+    const int row = it / CPR, c = (it % CPR) * Pol::CW;
+    *reinterpret_cast<u32x4*>(&sm.k[buf][row * FwdSmem<Pol, D>::KLD + c]) = r.k[i];
+  }
+}
+
+template <class Pol, int D>
+__device__ __forceinline__ void lds_put_v(FwdSmem<Pol, D>& sm, int buf, const TileRegs<Pol, D>& r) {
+  using SM = FwdSmem<Pol, D>;
+  constexpr int CPR = TileRegs<Pol, D>::CPR;
+  if constexpr (v_rowmajor<Pol>()) {
+#pragma unroll
+    for (int i = 0; i < TileRegs<Pol, D>::N; ++i) {
+      const int it = threadIdx.x + FWD_THREADS * i;
+      const int row = it / CPR, c = (it % CPR) * Pol::CW;
+      const u16x8 bits = __builtin_bit_cast(u16x8, r.v[i]);
+      f16x8 hv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = bf16_bits_to_f16(bits[e]);
+      *reinterpret_cast<f16x8*>(&sm.v[buf][row * SM::VLD + c]) = hv;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TileRegs<Pol, D>::N / 2; ++i) {
+      const int it = threadIdx.x + FWD_THREADS * i;
+      const int rp = it / CPR, c = (it % CPR) * Pol::CW;
+      float a[4], b[4];
+      __builtin_memcpy(a, &r.v[2 * i], 16);
+      __builtin_memcpy(b, &r.v[2 * i + 1], 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        typename Pol::vel_t* dst = &sm.v[buf][(c + e) * SM::VLD + 2 * rp];
+        dst[0] = a[e];
+        dst[1] = b[e];
+      }
+    }
+  }
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f16x4 lds_read_tr16(const _Float16* p) {
+  s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(f16x4, t);
+}
+
+// A operand of O^T = V^T P^T for d sub-tile dt, key sub-tile st, MFMA step s.
+// Element e of lane (row d, half h) is V[32 st + acc_row(KW s + e, h)][d].
+template <class Pol, int D>
+__device__ __forceinline__ typename Pol::vop_t load_v_op(const FwdSmem<Pol, D>& sm, int buf, int dt,
+                                                         int st, int s, int lane) {
+  using SM = FwdSmem<Pol, D>;
+  if constexpr (v_rowmajor<Pol>()) {
+    // ds_read_b64_tr_b16: within each 16-lane block, lane i receives element
+    // i % 4 of the 4-element chunks addressed by lanes 4e + i / 4 (e = 0..3).
+    // Lane L of a block therefore addresses row (row0 + L / 4), columns
+    // (dbase + 4 (L % 4)), which hands lane i the four keys row0 .. row0+3 of
+    // column dbase + i.
+    const int h = lane >> 5, blk = (lane >> 4) & 1, li = lane & 15;
+    const int row = 32 * st + 16 * s + 4 * h + (li >> 2);
+    const int cv = 32 * dt + 16 * blk + 4 * (li & 3);
+    const _Float16* base = &sm.v[buf][row * SM::VLD + cv];
+    const f16x4 lo = lds_read_tr16(base);
+    const f16x4 hi = lds_read_tr16(base + 8 * SM::VLD);
+    f16x8 a;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = lo[e];
+      a[4 + e] = hi[e];
+    }
+    return a;
+  } else {
+    return load_t_op<Pol>(sm.v[buf], SM::VLD, 32 * dt + (lane & 31), 32 * st, s, lane >> 5);
+  }
+}
+
+// Sum of the elements of a value operand, in fp32.
+__device__ __forceinline__ float vop_sum(const f16x8& x) {
+  const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 pr = {x[2 * i], x[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2(pr, one, acc, false);
+  }
+  return acc;
+}
+__device__ __forceinline__ float vop_sum(float x) { return x; }
+
+// Score MFMAs of one 32-key sub-tile: S^T and R^T (32 keys x 32 queries)
+// from the K rows at LDS buffer `buf`, sub-tile `st`.
+template <class Pol, int D>
+__device__ __forceinline__ void score_sub(const FwdSmem<Pol, D>& sm, int buf, int st, int col,
+                                          int half, const typename Pol::sop_t* qop,
+                                          const typename Pol::sop_t* rop, f32x16& sacc,
+                                          f32x16& racc) {
+  constexpr int KW = Pol::KW, KSTEP = Pol::KSTEP, NS = D / KSTEP;
+  const typename Pol::in_t* krow = &sm.k[buf][(32 * st + col) * FwdSmem<Pol, D>::KLD + KW * half];
+  {
+    const typename Pol::sop_t a = load_sop<Pol>(krow);
+    sacc = Pol::mma_s(a, qop[0], zero16());
+    racc = Pol::mma_s(a, rop[0], zero16());
+  }
+#pragma unroll
+  for (int s = 1; s < NS; ++s) {
+    const typename Pol::sop_t a = load_sop<Pol>(krow + KSTEP * s);
+    sacc = Pol::mma_s(a, qop[s], sacc);
+    racc = Pol::mma_s(a, rop[s], racc);
+  }
+}
+
+// Online-softmax state of one wave (one query per lane column).
+template <class Pol, int D>
+struct FwdState {
+  static constexpr int ND = D / 32;
+  f32x16 oacc[ND], uacc[ND];
+  // l / c: sums of the rounded operands (normalise O, U, C consistently);
+  // e: the unrounded sum, used only for the LSE.
+  float m_run, l_part, c_part, e_part;
+};
+
+// Softmax statistics of one 32-key sub-tile whose first key is `kbase`
+// (scores in sacc): causal mask, row max, and the rare lazy rescale.  Returns
+// the reference max the probabilities of this sub-tile are taken against.
+template <class Pol, int D>
+__device__ __forceinline__ float softmax_stats(FwdState<Pol, D>& S, int kbase, int qw, int my_q,
+                                               int half, float scale_log2, f32x16& sacc) {
+  constexpr int ND = D / 32;
+  // causal mask where the sub-tile reaches past the wave's first query
+  if (kbase + 31 > qw) {
+#pragma unroll
+    for (int a = 0; a < 16; ++a)
+      if (kbase + acc_row(a, half) > my_q) sacc[a] = -INFINITY;
+  }
+  float mt = -INFINITY;
+#pragma unroll
+  for (int a = 0; a < 16; ++a) mt = fmaxf(mt, sacc[a]);
+  mt = fmaxf(mt, xor32(mt)) * scale_log2;
+  // Lazy rescale: the reference max m_run only moves when some row's max
+  // exceeds it by more than kRescaleLog2 (so p <= 2^kRescaleLog2 in between);
+  // the final normalisation uses the same m_run, so the result is unchanged.
+  if (__any(mt > S.m_run + kRescaleLog2)) {
+    const float m_new = fmaxf(S.m_run, mt);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(S.m_run - m_use);
+    S.l_part *= alpha;
+    S.c_part *= alpha;
+    S.e_part *= alpha;
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        S.oacc[i][a] *= alpha;
+        S.uacc[i][a] *= alpha;
+      }
+    S.m_run = m_new;
+  }
+  return (S.m_run == -INFINITY) ? 0.f : S.m_run;
+}
+
+// Probabilities and value MFMAs of one 32-key sub-tile (straight-line code):
+// p = exp2(s * scale_log2 - m); P and P.R rounded to the value operand with
+// the row sums taken over exactly the rounded operands; then O^T += V^T P^T
+// and U^T += V^T (P.R)^T with V rows from LDS buffer `buf`, sub-tile `st`.
+// The V operand of step k+1 is read before the MFMAs of step k.
+template <class Pol, int D>
+__device__ __forceinline__ void softmax_pv_body(FwdState<Pol, D>& S, const FwdSmem<Pol, D>& sm,
+                                                int buf, int st, int lane, float scale_log2,
+                                                float m_use, const f32x16& sacc,
+                                                const f32x16& racc) {
+  using vop_t = typename Pol::vop_t;
+  constexpr int KW = Pol::KW, NV = 32 / Pol::KSTEP, ND = D / 32;
+  vop_t pop[NV], prop[NV];
+#pragma unroll
+  for (int s = 0; s < NV; ++s) {
+#pragma unroll
+    for (int e = 0; e < KW; ++e) {
+      const int a = KW * s + e;
+      const float p = fast_exp2(__builtin_fmaf(sacc[a], scale_log2, -m_use));
+      S.e_part += p;
+      set_elem(pop[s], e, Pol::round_v(p));
+      set_elem(prop[s], e, Pol::round_v(p * racc[a]));
+    }
+    S.l_part += vop_sum(pop[s]);
+    S.c_part += vop_sum(prop[s]);
+  }
+  vop_t av = load_v_op<Pol, D>(sm, buf, 0, st, 0, lane);
+#pragma unroll
+  for (int k = 0; k < NV * ND; ++k) {
+    const int s = k / ND, dt = k % ND;
+    vop_t an = av;
+    if (k + 1 < NV * ND) an = load_v_op<Pol, D>(sm, buf, (k + 1) % ND, st, (k + 1) / ND, lane);
+    S.oacc[dt] = Pol::mma_v(av, pop[s], S.oacc[dt]);
+    S.uacc[dt] = Pol::mma_v(av, prop[s], S.uacc[dt]);
+    av = an;
+  }
+}
+
+// One pipelined sub-tile step of the bf16 path, as a fixed instruction order
+// (sched_barrier sections):
+//   sections 0..NS-1: one score MFMA pair (S, R) of the NEXT sub-tile, with
+//     its K operand read two sections ahead, interleaved with the exp / p.r
+//     work of 16/NS elements of the CURRENT sub-tile;
+//   then the fp16 packing and row sums of the current sub-tile;
+//   then its value MFMAs (O, U), each V operand read one step ahead.
+// The next scores are computed unconditionally (for the last sub-tile they
+// read a valid but stale LDS buffer and are discarded).
+template <int D>
+__device__ __forceinline__ void subtile_step_bf16(FwdState<PolBF16, D>& S,
+                                                  const FwdSmem<PolBF16, D>& sm, int kbuf_next,
+                                                  int st_next, int vbuf, int st_cur, int col,
+                                                  int half, int lane, float scale_log2, float m_use,
+                                                  const bf16x8* qop, const bf16x8* rop,
+                                                  const f32x16& sc, const f32x16& rc, f32x16& sn,
+                                                  f32x16& rn) {
+  using SM = FwdSmem<PolBF16, D>;
+  constexpr int NS = D / 16;    // score MFMA steps
+  constexpr int ND = D / 32;    // value d sub-tiles
+  constexpr int EPS = 16 / NS;  // softmax elements per section
+  const uint16_t* krow = &sm.k[kbuf_next][(32 * st_next + col) * SM::KLD + 8 * half];
+  bf16x8 kb[NS];
+  float pv[16], prv[16];
+  kb[0] = load_sop<PolBF16>(krow);
+  kb[1] = load_sop<PolBF16>(krow + 16);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    if (i + 2 < NS) kb[i + 2] = load_sop<PolBF16>(krow + 16 * (i + 2));
+    sn = PolBF16::mma_s(kb[i], qop[i], i == 0 ? zero16() : sn);
+    rn = PolBF16::mma_s(kb[i], rop[i], i == 0 ? zero16() : rn);
+#pragma unroll
+    for (int e = 0; e < EPS; ++e) {
+      const int a = EPS * i + e;
+      const float p = fast_exp2(__builtin_fmaf(sc[a], scale_log2, -m_use));
+      S.e_part += p;
+      pv[a] = p;
+      prv[a] = p * rc[a];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  f16x8 pop[2], prop[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pop[s2][e] = (_Float16)pv[8 * s2 + e];
+      prop[s2][e] = (_Float16)prv[8 * s2 + e];
+    }
+    S.l_part += vop_sum(pop[s2]);
+    S.c_part += vop_sum(prop[s2]);
+  }
+  f16x8 av = load_v_op<PolBF16, D>(sm, vbuf, 0, st_cur, 0, lane);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < 2 * ND; ++k) {
+    const int s2 = k / ND, dt = k % ND;
+    f16x8 an = av;
+    if (k + 1 < 2 * ND) an = load_v_op<PolBF16, D>(sm, vbuf, (k + 1) % ND, st_cur, (k + 1) / ND, lane);
+    S.oacc[dt] = PolBF16::mma_v(av, pop[s2], S.oacc[dt]);
+    S.uacc[dt] = PolBF16::mma_v(av, prop[s2], S.uacc[dt]);
+    av = an;
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 template <class Pol, int D>
@@ -100,11 +396,9 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     float* __restrict__ vbar_aux, int B, int Hq, int Hkv, int T, float scale_log2) {
   using in_t = typename Pol::in_t;
   using sop_t = typename Pol::sop_t;
-  using vop_t = typename Pol::vop_t;
   constexpr int KW = Pol::KW, KSTEP = Pol::KSTEP;
-  constexpr int NS = D / KSTEP;     // score MFMA steps over d
-  constexpr int NV = 32 / KSTEP;    // value MFMA steps per 32-key sub-tile
-  constexpr int ND = D / 32;        // 32-row d sub-tiles of O^T / U^T
+  constexpr int NS = D / KSTEP;  // score MFMA steps over d
+  constexpr int ND = D / 32;     // 32-row d sub-tiles of O^T / U^T
 
   __shared__ FwdSmem<Pol, D> sm;
 
@@ -118,7 +412,9 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
   const int hk = h / (Hq / Hkv);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a scalar so that every per-wave tile condition below is a
+  // uniform (scalar) branch
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31;
   const int half = lane >> 5;
 
@@ -130,6 +426,16 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
   const in_t* rp = rho + ((size_t)bh * T) * D;
   const in_t* kp = k + ((size_t)(b * Hkv + hk) * T) * D;
   const in_t* vp = v + ((size_t)(b * Hkv + hk) * T) * D;
+
+  const int kend = min(T, q0 + FWD_BR);
+  const int ntiles = (kend + FWD_BC - 1) / FWD_BC;
+  // 32-key sub-tiles this wave attends to: keys [0, min(kend, qw + 32))
+  const int nsub = (min(kend, qw + 32) + 31) / 32;
+
+  // prologue: K(0), K(1), V(0) into LDS
+  TileRegs<Pol, D> pre;
+  gload_k<Pol, D>(pre, kp, 0, T);
+  gload_v<Pol, D>(pre, vp, 0, T);
 
   // Q and rho rows of this lane's query as B operands.
   sop_t qop[NS], rop[NS];
@@ -143,113 +449,74 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
       rop[s] = zero_sop<Pol>();
     }
   }
+  lds_put_k<Pol, D>(sm, 0, pre);
+  lds_put_v<Pol, D>(sm, 0, pre);
+  if (ntiles > 1) {
+    gload_k<Pol, D>(pre, kp, FWD_BC, T);
+    lds_put_k<Pol, D>(sm, 1, pre);
+  }
+  __syncthreads();
 
-  f32x16 oacc[ND], uacc[ND];
+  FwdState<Pol, D> S;
 #pragma unroll
   for (int i = 0; i < ND; ++i) {
-    oacc[i] = zero16();
-    uacc[i] = zero16();
+    S.oacc[i] = zero16();
+    S.uacc[i] = zero16();
   }
-  // l_part / c_part: sums of the rounded operands (normalise O, U, C
-  // consistently); e_part: the unrounded sum, used only for the LSE.
-  float m_run = -INFINITY, l_part = 0.f, c_part = 0.f, e_part = 0.f;
+  S.m_run = -INFINITY;
+  S.l_part = S.c_part = S.e_part = 0.f;
 
-  const int kend = min(T, q0 + FWD_BR);
-  const int ntiles = (kend + FWD_BC - 1) / FWD_BC;
+  // Software pipeline over 32-key sub-tiles t: the score MFMAs of t+1 are
+  // issued before the softmax and value MFMAs of t.
+  // Two score register sets with fixed roles: set A holds the even sub-tile
+  // 2j, set B the odd sub-tile 2j+1 of 64-key iteration j.  With kPipe the
+  // scores of the next sub-tile are issued before the softmax of the current.
+  constexpr bool kPipe = v_rowmajor<Pol>();
+  f32x16 sa, ra, sb, rb;
+  if constexpr (kPipe) score_sub<Pol, D>(sm, 0, 0, col, half, qop, rop, sa, ra);
+  __syncthreads();  // K(0) fully read before iteration 0 may refill its buffer
 
   for (int j = 0; j < ntiles; ++j) {
     const int key0 = j * FWD_BC;
-    __syncthreads();
-    stage_kv_tile<Pol, D>(sm, kp, vp, key0, T);
-    __syncthreads();
-    if (key0 > qw + 31) continue;  // every key of the tile is after every query of the wave
-
-    f32x16 sacc[2], racc[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      sacc[st] = zero16();
-      racc[st] = zero16();
-      const in_t* krow = &sm.k[(32 * st + col) * FwdSmem<Pol, D>::KLD + KW * half];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        sop_t a = load_sop<Pol>(krow + KSTEP * s);
-        sacc[st] = Pol::mma_s(a, qop[s], sacc[st]);
-        racc[st] = Pol::mma_s(a, rop[s], racc[st]);
+    const bool has_next_k = j + 2 < ntiles;
+    const bool has_next_v = j + 1 < ntiles;
+    if (has_next_k) gload_k<Pol, D>(pre, kp, key0 + 2 * FWD_BC, T);
+    if (has_next_v) gload_v<Pol, D>(pre, vp, key0 + FWD_BC, T);
+    const int t0 = 2 * j;
+    if constexpr (kPipe) {
+      // sub-tile 2j (set A) while the scores of 2j+1 (set B) are computed
+      if (t0 < nsub) {
+        const float m_use = softmax_stats<Pol, D>(S, key0, qw, my_q, half, scale_log2, sa);
+        subtile_step_bf16<D>(S, sm, j & 1, 1, j & 1, 0, col, half, lane, scale_log2, m_use, qop, rop,
+                             sa, ra, sb, rb);
+      }
+      // sub-tile 2j+1 (set B) while the scores of 2j+2 (set A) are computed
+      if (t0 + 1 < nsub) {
+        const float m_use = softmax_stats<Pol, D>(S, key0 + 32, qw, my_q, half, scale_log2, sb);
+        subtile_step_bf16<D>(S, sm, (j + 1) & 1, 0, j & 1, 1, col, half, lane, scale_log2, m_use,
+                             qop, rop, sb, rb, sa, ra);
+      }
+    } else {
+      if (t0 < nsub) {
+        score_sub<Pol, D>(sm, j & 1, 0, col, half, qop, rop, sa, ra);
+        const float m_use = softmax_stats<Pol, D>(S, key0, qw, my_q, half, scale_log2, sa);
+        softmax_pv_body<Pol, D>(S, sm, j & 1, 0, lane, scale_log2, m_use, sa, ra);
+      }
+      if (t0 + 1 < nsub) {
+        score_sub<Pol, D>(sm, j & 1, 1, col, half, qop, rop, sb, rb);
+        const float m_use = softmax_stats<Pol, D>(S, key0 + 32, qw, my_q, half, scale_log2, sb);
+        softmax_pv_body<Pol, D>(S, sm, j & 1, 1, lane, scale_log2, m_use, sb, rb);
       }
     }
-
-    // causal mask on the tiles that reach past the wave's first query
-    if (key0 + FWD_BC - 1 > qw) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const int key = key0 + 32 * st + acc_row(a, half);
-          if (key > my_q) sacc[st][a] = -INFINITY;
-        }
-    }
-
-    float mt = -INFINITY;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int a = 0; a < 16; ++a) mt = fmaxf(mt, sacc[st][a]);
-    mt = fmaxf(mt, xor32(mt));
-    const float m_new = fmaxf(m_run, mt * scale_log2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-
-    // p = exp2(s * scale_log2 - m); P and P.R rounded to the value operand,
-    // and the row sums taken over exactly the rounded operands.
-    float lsum = 0.f, csum = 0.f, esum = 0.f;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        const float p = fast_exp2(__builtin_fmaf(sacc[st][a], scale_log2, -m_use));
-        esum += p;
-        const auto pv = Pol::round_v(p);
-        const auto prv = Pol::round_v(p * racc[st][a]);
-        lsum += Pol::vel_to_f32(pv);
-        csum += Pol::vel_to_f32(prv);
-        sacc[st][a] = Pol::vel_to_f32(pv);
-        racc[st][a] = Pol::vel_to_f32(prv);
-      }
-    l_part = alpha * l_part + lsum;
-    c_part = alpha * c_part + csum;
-    e_part = alpha * e_part + esum;
-#pragma unroll
-    for (int i = 0; i < ND; ++i)
-#pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        oacc[i][a] *= alpha;
-        uacc[i][a] *= alpha;
-      }
-
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int s = 0; s < NV; ++s) {
-        vop_t pop, prop;
-#pragma unroll
-        for (int e = 0; e < KW; ++e) {
-          set_elem(pop, e, Pol::round_v(sacc[st][KW * s + e]));
-          set_elem(prop, e, Pol::round_v(racc[st][KW * s + e]));
-        }
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
-          vop_t a = load_vt_op<Pol, D>(sm, 32 * dt + col, st, s, half);
-          oacc[dt] = Pol::mma_v(a, pop, oacc[dt]);
-          uacc[dt] = Pol::mma_v(a, prop, uacc[dt]);
-        }
-      }
+    if (has_next_k) lds_put_k<Pol, D>(sm, j & 1, pre);
+    if (has_next_v) lds_put_v<Pol, D>(sm, (j + 1) & 1, pre);
+    __syncthreads();
   }
 
   // epilogue: o = (O/l)(1 + C/l) - U/l ; LSE = ln sum exp(scaled scores)
-  const float l_tot = l_part + xor32(l_part);
-  const float c_tot = c_part + xor32(c_part);
-  const float e_tot = e_part + xor32(e_part);
+  const float l_tot = S.l_part + xor32(S.l_part);
+  const float c_tot = S.c_part + xor32(S.c_part);
+  const float e_tot = S.e_part + xor32(S.e_part);
   const float inv = 1.f / l_tot;
   const float cc = c_tot * inv;
   if (my_q < T) {
@@ -263,15 +530,15 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
         f32x4 ov, vv;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const float vbar = oacc[dt][4 * i + jj] * inv;
+          const float vbar = S.oacc[dt][4 * i + jj] * inv;
           vv[jj] = vbar;
-          ov[jj] = vbar * (1.f + cc) - uacc[dt][4 * i + jj] * inv;
+          ov[jj] = vbar * (1.f + cc) - S.uacc[dt][4 * i + jj] * inv;
         }
         *reinterpret_cast<f32x4*>(orow + d0) = ov;
         if (vrow) *reinterpret_cast<f32x4*>(vrow + d0) = vv;
       }
     if (half == 0) {
-      if (lse) lse[(size_t)bh * T + my_q] = (m_run + __log2f(e_tot)) * kLn2;
+      if (lse) lse[(size_t)bh * T + my_q] = (S.m_run + __log2f(e_tot)) * kLn2;
       if (c_aux) c_aux[(size_t)bh * T + my_q] = cc;
     }
   }
