@@ -79,11 +79,12 @@ __device__ __forceinline__ void gload_k(TileRegs<Pol, D>& r, const typename Pol:
   for (int i = 0; i < TileRegs<Pol, D>::N; ++i) {
     const int it = threadIdx.x + FWD_THREADS * i;
     const int row = it / CPR, c = (it % CPR) * Pol::CW;
-    const int key = key0 + row;
-    // clamped in-bounds load, zeroed past T (no divergent branch)
-    const u32x4 val = *reinterpret_cast<const u32x4*>(kb + (size_t)min(key, T - 1) * D + c);
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    r.k[i] = key < T ? val : z;
+    // Rows past T load row T-1 instead (in bounds, finite).  Those keys are
+    // after every valid query, so the causal mask gives them p = 0 and their
+    // (finite) K and V contribute nothing; no select on the loaded value, so
+    // the load's wait can stay at the LDS write.
+    const int key = min(key0 + row, T - 1);
+    r.k[i] = *reinterpret_cast<const u32x4*>(kb + (size_t)key * D + c);
   }
 }
 
@@ -98,10 +99,8 @@ __device__ __forceinline__ void gload_v(TileRegs<Pol, D>& r, const typename Pol:
     for (int i = 0; i < TileRegs<Pol, D>::N; ++i) {
       const int it = threadIdx.x + FWD_THREADS * i;
       const int row = it / CPR, c = (it % CPR) * Pol::CW;
-      const int key = key0 + row;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(vb + (size_t)min(key, T - 1) * D + c);
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      r.v[i] = key < T ? val : z;
+      const int key = min(key0 + row, T - 1);  // past T: row T-1, masked (see gload_k)
+      r.v[i] = *reinterpret_cast<const u32x4*>(vb + (size_t)key * D + c);
     }
   } else {
 #pragma unroll
@@ -344,7 +343,8 @@ __device__ __forceinline__ void subtile_step_bf16(FwdState<PolBF16, D>& S,
   constexpr int EPS = 16 / NS;  // softmax elements per section
   const uint16_t* krow = &sm.k[kbuf_next][(32 * st_next + col) * SM::KLD + 8 * half];
   bf16x8 kb[NS];
-  float pv[16], prv[16];
+  f16x8 pop[2], prop[2];
+  float lsum = 0.f, csum = 0.f;
   kb[0] = load_sop<PolBF16>(krow);
   kb[1] = load_sop<PolBF16>(krow + 16);
   __builtin_amdgcn_sched_barrier(0);
@@ -353,27 +353,27 @@ __device__ __forceinline__ void subtile_step_bf16(FwdState<PolBF16, D>& S,
     if (i + 2 < NS) kb[i + 2] = load_sop<PolBF16>(krow + 16 * (i + 2));
     sn = PolBF16::mma_s(kb[i], qop[i], i == 0 ? zero16() : sn);
     rn = PolBF16::mma_s(kb[i], rop[i], i == 0 ? zero16() : rn);
+    // exp / p.r of EPS elements, packed to fp16 pairs as they are produced
 #pragma unroll
-    for (int e = 0; e < EPS; ++e) {
+    for (int e = 0; e < EPS; e += 2) {
       const int a = EPS * i + e;
-      const float p = fast_exp2(__builtin_fmaf(sc[a], scale_log2, -m_use));
-      S.e_part += p;
-      pv[a] = p;
-      prv[a] = p * rc[a];
+      const float p0 = fast_exp2(__builtin_fmaf(sc[a], scale_log2, -m_use));
+      const float p1 = fast_exp2(__builtin_fmaf(sc[a + 1], scale_log2, -m_use));
+      S.e_part += p0 + p1;
+      const f16x2 ph = {(_Float16)p0, (_Float16)p1};
+      const f16x2 rh = {(_Float16)(p0 * rc[a]), (_Float16)(p1 * rc[a + 1])};
+      const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+      lsum = __builtin_amdgcn_fdot2(ph, one, lsum, false);
+      csum = __builtin_amdgcn_fdot2(rh, one, csum, false);
+      pop[a >> 3][a & 7] = ph[0];
+      pop[a >> 3][(a & 7) + 1] = ph[1];
+      prop[a >> 3][a & 7] = rh[0];
+      prop[a >> 3][(a & 7) + 1] = rh[1];
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  f16x8 pop[2], prop[2];
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pop[s2][e] = (_Float16)pv[8 * s2 + e];
-      prop[s2][e] = (_Float16)prv[8 * s2 + e];
-    }
-    S.l_part += vop_sum(pop[s2]);
-    S.c_part += vop_sum(prop[s2]);
-  }
+  S.l_part += lsum;
+  S.c_part += csum;
   f16x8 av = load_v_op<PolBF16, D>(sm, vbuf, 0, st_cur, 0, lane);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
