@@ -91,7 +91,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq_kernel(
 
   const int nqb = (T + DQ_BR - 1) / DQ_BR;
   const int bh_count = B * Hq;
-  const int lin = blockIdx.x;
+  const int lin = xcd_block_order(blockIdx.x, bh_count, nqb * bh_count);
   const int qb = nqb - 1 - lin / bh_count;
   const int bh = lin % bh_count;
   const int b = bh / Hq, h = bh % Hq;

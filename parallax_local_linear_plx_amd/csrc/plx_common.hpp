@@ -134,6 +134,20 @@ __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Block order for a grid whose blocks enumerate (level, slot) with `slots`
+// consecutive slots per level.  Consecutive block ids are dispatched round-
+// robin to the 8 XCDs (each with its own L2), so without remapping every XCD
+// sees every slot.  The remap gives XCD x the contiguous slot range
+// [x*slots/8, (x+1)*slots/8) at every level (neighbouring heads share K/V),
+// keeping each level's blocks in order.  Identity when slots or the grid is
+// not a multiple of 8.
+__device__ __forceinline__ int xcd_block_order(int id, int slots, int total) {
+  if ((slots & 7) != 0 || (total & 7) != 0) return id;
+  const int x = id & 7, m = id >> 3;
+  const int per = slots >> 3;
+  return (m / per) * slots + x * per + (m % per);
+}
+
 // Cooperative copy of ROWS rows of D elements (rows at or beyond `nvalid` read
 // as zero) into a row-major LDS tile with row stride `ld` (elements).
 template <class Pol, int D, int ROWS, int NT>

@@ -405,7 +405,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
   // Longest causal rows first: block x enumerates (q-block descending, b*h).
   const int nqb = (T + FWD_BR - 1) / FWD_BR;
   const int bh_count = B * Hq;
-  const int lin = blockIdx.x;
+  const int lin = xcd_block_order(blockIdx.x, bh_count, nqb * bh_count);
   const int qb = nqb - 1 - lin / bh_count;
   const int bh = lin % bh_count;
   const int b = bh / Hq, h = bh % Hq;
