@@ -14,7 +14,8 @@ stream), W warm-up steps, then exactly K timed steps between two device
 synchronisations.  The CPU baseline is the fp64 oracle on a bounded sample of
 prefill rows, timed on the host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|decode|train|all]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+                       [--only all|prefill|decode|decode_long|train|copy] [--no-cpu]
 """
 
 from __future__ import annotations
@@ -161,6 +162,58 @@ def bench_train(steps, warmup):
     return out
 
 
+# -------------------------------------------------------- copy calibration
+def bench_copy(steps, nbytes=1 << 30):
+    """A plain device-to-device copy of a known size.  Run under rocprofv3
+    --pmc FETCH_SIZE / WRITE_SIZE, it gives the factor between those counters
+    and true bytes on this GPU, which scales the kernels' counter readings."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = time_steps(lambda: dst.copy_(src), steps, 1)
+    return {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms": ms,
+            "GB/s": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
+# ------------------------------------------------------------------ traffic
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "prefill": ["plx_fwd.hip", "plx_common.hpp"],
+    "decode": ["plx_decode.hip", "plx_common.hpp"],
+}
+
+
+def source_digest(key):
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[key]:
+        with open(os.path.join(ROOT, "parallax_local_linear_plx_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key):
+    """HBM bytes per launch of the dominant kernel, from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE scaled by the copy calibration), or None
+    when no summary exists or the kernel source changed since it was taken."""
+    path = os.path.join(TRAFFIC_DIR, f"traffic_{key}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for ln in open(path):
+        if ":" in ln:
+            k, v = ln.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_digest") != source_digest(key):
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
 # ------------------------------------------------------------- CPU baseline
 def cpu_baseline(budget_s=12.0):
     """The fp64 oracle on sampled rows of the prefill workload, on host cores.
@@ -198,9 +251,13 @@ def cpu_baseline(budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "train"])
+    # The GPU raises its clocks only after tens of milliseconds of sustained
+    # work, so the default warm-up is long enough (>= ~40 ms per workload) to
+    # time the steady state rather than the ramp.
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--only", default="all",
+                    choices=["all", "prefill", "decode", "decode_long", "train", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -223,11 +280,15 @@ def main():
         log("prefill ...")
         res["prefill"] = bench_prefill(args.steps, args.warmup)
         log(f"  {res['prefill']['ms'] * 1e3:.1f} us  {res['prefill']['tflops']:.1f} TFLOP/s")
+    if args.only == "copy":
+        print(json.dumps(bench_copy(args.steps)), flush=True)
+        return
     if args.only in ("all", "decode"):
         log("decode B64 ctx8192 ...")
         res["decode"] = bench_decode(args.steps, args.warmup, 64, [8192] * 64, 8192,
                                      "bf16 decode B=64 Hq=16 Hkv=8 ctx=8192 d=128", 31)
         log(f"  {res['decode']['us_per_step']:.1f} us  {res['decode']['GB/s']:.0f} GB/s")
+    if args.only in ("all", "decode_long"):
         from parallax_local_linear_plx_amd import inputs
 
         ctx = inputs.long_decode_ctx()
@@ -250,7 +311,8 @@ def main():
                      "config": p["config"],
                      "roofline": {"bound": "mfma", "achieved": round(p["tflops"], 2),
                                   "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                  "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                  "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4),
+                                  "traffic": measured_traffic("prefill"),
                                   "kernel": "fwd_kernel<PolBF16,128>",
                                   "algorithmic_flops_per_launch": p["flops"]}})
     else:
@@ -258,6 +320,14 @@ def main():
     for key in ("decode", "decode_long", "train"):
         if key in res:
             line[key] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res[key].items()}
+            if key.startswith("decode"):
+                r = res[key]
+                line[key]["roofline"] = {
+                    "bound": "hbm", "achieved": round(r["GB/s"], 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(r["GB/s"] / PEAK_HBM_GBS, 4),
+                    "traffic": measured_traffic("decode") if key == "decode" else None,
+                    "kernel": "decode16_partial_kernel<128,2> + decode_merge_kernel",
+                    "algorithmic_bytes_per_launch": r["bytes"]}
     if not args.no_cpu and args.only in ("all", "prefill"):
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline()

@@ -627,12 +627,16 @@ hipError_t launch_decode_t(const void* q, const void* rho, const void* kc, const
 
 }  // namespace
 
-// Automatic split count: chunks of 2048 keys, halved (down to 256) until the
-// grid has at least ~8 workgroups per compute unit.
+// Split count: as few splits as give two workgroups per compute unit.  The
+// partial kernel is bound by the loads each wave keeps in flight, and a long
+// chunk keeps every wave streaming; more splits only add merge traffic and
+// per-workgroup start-up.  Chunks stay at least 256 keys long.
 int decode_auto_splits(int B, int Hkv, int S_max) {
-  int chunk = 2048;
-  while (chunk > 256 && (long long)B * Hkv * ((S_max + chunk - 1) / chunk) < 2048) chunk >>= 1;
-  return (S_max + chunk - 1) / chunk;
+  const long long slots = (long long)B * Hkv;
+  long long ns = (512 + slots - 1) / slots;
+  const long long max_ns = (S_max + 255) / 256;
+  if (ns > max_ns) ns = max_ns;
+  return ns < 1 ? 1 : (int)ns;
 }
 
 // Keys per split: S_max / num_splits rounded up to whole workgroup steps.
