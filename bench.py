@@ -326,7 +326,7 @@ def main():
                     "bound": "hbm", "achieved": round(r["GB/s"], 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(r["GB/s"] / PEAK_HBM_GBS, 4),
                     "traffic": measured_traffic("decode") if key == "decode" else None,
-                    "kernel": "decode16_partial_kernel<128,2> + decode_merge_kernel",
+                    "kernel": "decode16_balanced_kernel<128,2> + decode_merge_balanced_kernel<128>",
                     "algorithmic_bytes_per_launch": r["bytes"]}
     if not args.no_cpu and args.only in ("all", "prefill"):
         log("cpu baseline (oracle) ...")

@@ -99,12 +99,20 @@ plx_status plx_fwd_prefill(const void* q, const void* k, const void* v, const vo
  * Decode: one new query and probe per (b, h) against a KV cache.
  *
  * Query (b, h) attends to the cache rows [0, ctx_len[b]) of KV head h/(Hq/Hkv)
- * (the cache already holds the current token; no mask).  The key range of every
- * sequence is cut into splits processed by separate workgroups, each producing a
- * partial record (m, l, O, U, Kbar) -- running max, sum, P V, (P . R) V and P K --
+ * (the cache already holds the current token; no mask).  The keys are cut into
+ * ranges processed by separate workgroups, each producing a partial record
+ * (m, l, C, O, U) -- running max, sum of P, sum of P . R, P V and (P . R) V --
  * which a second kernel merges:
- *   M = max m_s, a_s = exp(m_s - M), l = sum a_s l_s, O/U/Kbar likewise,
- *   o = (O/l)(1 + (Kbar . rho)/l) - U/l,   LSE = M + ln l.
+ *   M = max m_s, a_s = exp(m_s - M), l = sum a_s l_s, C/O/U likewise,
+ *   o = (O/l)(1 + C/l) - U/l,   LSE = M + ln l.
+ * C/l equals kbar . rho (kbar = P K / l), the only use the output makes of the
+ * mean key, so the record carries that scalar instead of the vector P K.
+ *
+ * num_splits = 0 (bf16): the (b, kv head, key) space of all sequences, laid end
+ * to end, is cut into equal contiguous ranges, one per workgroup (at most 512,
+ * two per compute unit), so ragged lengths keep every workgroup equally busy.
+ * num_splits > 0, or fp32: every sequence's [0, S_max) is cut into num_splits
+ * equal splits (fp32 with 0 picks the count automatically).
  *
  *   q, rho        [B, Hq, d]          dtype
  *   k_cache       [B, Hkv, S_max, d]  dtype
@@ -114,7 +122,7 @@ plx_status plx_fwd_prefill(const void* q, const void* k, const void* v, const vo
  *                 cache row is ever read).
  *   o             [B, Hq, d] fp32, written
  *   lse           [B, Hq] fp32, or NULL
- *   num_splits    number of key splits over S_max, 0 = automatic
+ *   num_splits    0 = automatic (see above), else the number of key splits over S_max
  *   workspace     device scratch of at least plx_decode_workspace_size(...) bytes,
  *                 16-byte aligned; contents on entry are ignored
  * Requires group = Hq / Hkv in {1, 2, 4, 8, 16}.  Rows of the cache at or beyond

@@ -8,15 +8,17 @@
 // the Russian write-up's caption contrasts a variant tuned for parallel
 // decoding, read here as splitting each sequence's keys over workgroups.
 //
-// Kernel 1 (partial): workgroup = (split, kv head, b).  The query heads that
-// share the KV head are stacked with their probes as the 2G columns
-// [q_0, rho_0, q_1, rho_1, ...] of one MFMA B operand, so each K row is read
-// once for all of them:  S^T = K [q;rho]^T  gives scores (even columns) and
-// r = rho . k (odd columns) in one MFMA chain.  Per split it accumulates
-//   m, l = sum p, O = sum p v, U = sum (p r) v, Kbar = sum p k
-// and writes one partial record per query head.
+// Kernel 1 (partial): a workgroup takes a range of one sequence's keys.  The
+// query heads that share the KV head are stacked with their probes as the 2G
+// columns [q_0, rho_0, q_1, rho_1, ...] of one MFMA B operand, so each K row is
+// read once for all of them:  S^T = K [q;rho]^T  gives scores (even columns)
+// and r = rho . k (odd columns) in one MFMA chain.  Per range it accumulates
+//   m, l = sum p, C = sum p r, O = sum p v, U = sum (p r) v
+// and writes one partial record per query head.  C / l equals kbar . rho
+// exactly (kbar = sum_j w_j k_j), so the scalar C carries everything of the
+// mean key the output needs, and it merges across ranges like l.
 // Kernel 2 (merge): per (b, h) rescales the records to a common max and
-// finishes  o = (O/l)(1 + (Kbar . rho)/l) - U/l,  LSE = M + ln l.
+// finishes  o = (O/l)(1 + C/l) - U/l,  LSE = M + ln l.
 #include "plx_common.hpp"
 #include "plx_kernels.hpp"
 
@@ -35,11 +37,9 @@ struct DecSmem {
   using vel_t = typename Pol::vel_t;
   static constexpr int MLD = D + 1;  // merge buffer row stride (floats)
   static constexpr size_t TILE_BYTES = (size_t)DEC_WAVES * 2 * D * DEC_TLD * sizeof(vel_t);
-  static constexpr size_t MERGE_BYTES = (size_t)2 * 32 * MLD * sizeof(float);
-  static constexpr size_t BYTES = TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES;
   union {
-    vel_t tiles[DEC_WAVES][2][D * DEC_TLD];  // per wave: K^T then V^T
-    float merge[2][32 * MLD];                // [O/U, Kbar] x column x d
+    vel_t tiles[DEC_WAVES][D * DEC_TLD];  // per wave: V^T
+    float merge[32 * MLD];                // [O | U] x column x d
   };
   float mw[DEC_WAVES][32];
   float lsum[32];
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
   constexpr int NS = D / KSTEP;
   constexpr int NV = DEC_SUB / KSTEP;
   constexpr int ND = D / 32;
-  constexpr int REC = 3 * D + 4;
+  constexpr int REC = 2 * D + 4;
 
   __shared__ DecSmem<Pol, D> sm;
 
@@ -99,17 +99,13 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
 
   const in_t* kbase = kc + ((size_t)(b * Hkv + hk) * S_max) * D;
   const in_t* vbase = vc + ((size_t)(b * Hkv + hk) * S_max) * D;
-  vel_t* kt = sm.tiles[wave][0];
-  vel_t* vt = sm.tiles[wave][1];
+  vel_t* vt = sm.tiles[wave];
 
-  f32x16 ou[ND], kb[ND];
+  f32x16 ou[ND];
 #pragma unroll
-  for (int i = 0; i < ND; ++i) {
-    ou[i] = zero16();
-    kb[i] = zero16();
-  }
-  // l_part: sum of the rounded operands (normalises O, U, Kbar);
-  // e_part: the unrounded sum, used only for the LSE.
+  for (int i = 0; i < ND; ++i) ou[i] = zero16();
+  // l_part: sum of the rounded operands (normalises O and U; in the odd
+  // columns it is C); e_part: the unrounded sum, used only for the LSE.
   float m_run = -INFINITY, l_part = 0.f, e_part = 0.f;
 
   for (int g0 = k_begin; g0 < k_end; g0 += DEC_GROUP_KEYS) {
@@ -134,21 +130,17 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
 #pragma unroll
     for (int s = 0; s < NS; ++s) sacc = Pol::mma_s(kop[s], bop[s], sacc);
 
-    // K and V rows -> transposed per-wave tiles (value-operand type)
+    // V rows -> transposed per-wave tile (value-operand type)
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int e = 0; e < KW; ++e) {
         const int d = KSTEP * s + KW * half + e;
-        in_t kx, vx;
-        if constexpr (KW == 1) {
-          kx = kop[s];
+        in_t vx;
+        if constexpr (KW == 1)
           vx = vop[s];
-        } else {
-          kx = __builtin_bit_cast(u16x8, kop[s])[e];
+        else
           vx = __builtin_bit_cast(u16x8, vop[s])[e];
-        }
-        kt[d * DEC_TLD + col] = Pol::to_vel(kx);
         vt[d * DEC_TLD + col] = Pol::to_vel(vx);
       }
 
@@ -184,10 +176,7 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
 #pragma unroll
     for (int i = 0; i < ND; ++i)
 #pragma unroll
-      for (int a = 0; a < 16; ++a) {
-        ou[i][a] *= alpha;
-        kb[i][a] *= alpha;
-      }
+      for (int a = 0; a < 16; ++a) ou[i][a] *= alpha;
 
     wave_lds_sync();
 #pragma unroll
@@ -197,16 +186,11 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
       for (int e = 0; e < KW; ++e) set_elem(pop, e, Pol::round_v(sv[KW * s + e]));
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
-        vop_t av, ak;
+        vop_t av;
         const int drow = (32 * dt + col) * DEC_TLD;
 #pragma unroll
-        for (int e = 0; e < KW; ++e) {
-          const int key = acc_row(KW * s + e, half);
-          set_elem(av, e, vt[drow + key]);
-          set_elem(ak, e, kt[drow + key]);
-        }
+        for (int e = 0; e < KW; ++e) set_elem(av, e, vt[drow + acc_row(KW * s + e, half)]);
         ou[dt] = Pol::mma_v(av, pop, ou[dt]);
-        kb[dt] = Pol::mma_v(ak, pop, kb[dt]);
       }
     }
     wave_lds_sync();
@@ -215,8 +199,7 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
   // ---- merge the four waves' states through LDS ----
   __syncthreads();
   if (half == 0) sm.mw[wave][col] = m_run;
-  for (int i = threadIdx.x; i < 2 * 32 * DecSmem<Pol, D>::MLD; i += DEC_THREADS)
-    (&sm.merge[0][0])[i] = 0.f;
+  for (int i = threadIdx.x; i < 32 * DecSmem<Pol, D>::MLD; i += DEC_THREADS) sm.merge[i] = 0.f;
   if (threadIdx.x < 32) {
     sm.lsum[threadIdx.x] = 0.f;
     sm.esum[threadIdx.x] = 0.f;
@@ -237,13 +220,12 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
       const int d = 32 * dt + acc_row(a, half);
-      atomicAdd(&sm.merge[0][col * DecSmem<Pol, D>::MLD + d], ou[dt][a] * sc);
-      atomicAdd(&sm.merge[1][col * DecSmem<Pol, D>::MLD + d], kb[dt][a] * sc);
+      atomicAdd(&sm.merge[col * DecSmem<Pol, D>::MLD + d], ou[dt][a] * sc);
     }
   __syncthreads();
 
-  // record of head g: [m, l, e, 0, O[D], U[D], Kbar[D]]  (m in log2 units;
-  // l the rounded-operand sum, e the unrounded sum)
+  // record of head g: [m, l, e, C, O[D], U[D]]  (m in log2 units; l the
+  // rounded-operand sum, e the unrounded sum; C the odd column's rounded sum)
   for (int g = 0; g < G; ++g) {
     float* rec = part + (((size_t)b * Hq + hk * G + g) * nsplit + split) * REC;
     const int c0 = 2 * g;
@@ -253,110 +235,145 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
       rec[0] = M0;
       rec[1] = sm.lsum[c0];
       rec[2] = sm.esum[c0];
-      rec[3] = 0.f;
+      rec[3] = sm.lsum[c0 + 1];
     }
     for (int d = threadIdx.x; d < D; d += DEC_THREADS) {
-      rec[4 + d] = sm.merge[0][c0 * DecSmem<Pol, D>::MLD + d];
-      rec[4 + D + d] = sm.merge[0][(c0 + 1) * DecSmem<Pol, D>::MLD + d];
-      rec[4 + 2 * D + d] = sm.merge[1][c0 * DecSmem<Pol, D>::MLD + d];
+      rec[4 + d] = sm.merge[c0 * DecSmem<Pol, D>::MLD + d];
+      rec[4 + D + d] = sm.merge[(c0 + 1) * DecSmem<Pol, D>::MLD + d];
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// bf16 partial kernel on 16x16x32 MFMA tiles.
+// bf16 partial kernels on 16x16x32 MFMA tiles.
 //
 // Per wave and 32-key sub-tile: the K rows (loaded straight into A-operand
 // registers, bf16) give S^T = K [q;rho]^T over 16 columns (2 per head, up to 8
-// heads); K and V are then staged in the wave's LDS tile as fp16 rows and
-// read back transposed (ds_read_b64_tr_b16) as the A operands of
-//   [O|U]^T += V^T [p | p.r]^T   and   Kbar^T += K^T [p | p.r]^T.
-// The next sub-tile's loads are issued as soon as the current one is staged.
+// heads); the raw V rows are then staged in the wave's LDS tile and read
+// back transposed (ds_read_b64_tr_b16), converted to fp16, as the A operand of
+//   [O|U]^T += V^T [p | p.r]^T.
+// DEC_NSET register sets of loads rotate: a set's next loads go out as soon
+// as it has been staged, so a sub-tile's loads are in flight while the
+// previous one is computed.
 // Lane layout of a 16x16 accumulator: acc[j] is row 4*g + j, column l % 16,
 // with g = l / 16 the 16-lane group.
+//
+// Two schedules share the per-range body:
+//   chunked  : workgroup (split, kv head, b) takes keys [split*chunk, ...)
+//              of one sequence (the caller's explicit split count);
+//   balanced : the (b, kv head, key) space of all valid sequences, laid end to
+//              end, is cut into DEC_BAL_CTAS equal contiguous ranges, one per
+//              workgroup.  A range may span several (b, kv head) segments and
+//              writes one record set per segment piece, at slot = workgroup +
+//              segment index (unique, since pieces are ordered by both).  Every
+//              workgroup streams the same number of keys whatever the mix of
+//              context lengths.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
+// Register sets of loads in flight per wave.  One set (16 KB per wave, eight
+// waves per compute unit) already streams at the rate this grid reaches with
+// loads alone; a second set measured no faster and needs the registers the
+// occupancy of two workgroups per compute unit depends on.
+constexpr int DEC_NSET = 1;
+constexpr int DEC_BAL_CTAS = 512;  // balanced schedule: at most two workgroups per compute unit
+
 template <int D>
 struct Dec16Smem {
-  static constexpr int LD = D + 16;  // fp16 row stride: 8 rows of one transpose read hit 8 bank groups
+  static constexpr int LD = D + 16;  // row stride: 8 rows of one transpose read hit 8 bank groups
   static constexpr size_t TILE = (size_t)32 * LD;
   static constexpr int MLD = D + 1;
   union {
-    _Float16 tiles[DEC_WAVES][2][TILE];  // per wave: K rows, V rows
-    float merge[2][16 * MLD];            // [O/U, Kbar] x column x d
+    uint16_t tiles[DEC_WAVES][TILE];  // per wave: raw bf16 V rows
+    float merge[16 * MLD];            // [O | U] x column x d
   };
+  uint16_t bq[16 * D];  // score B operand: [column][d]
   float mw[DEC_WAVES][16];
   float lsum[16];
   float esum[16];
 };
 
-__device__ __forceinline__ f16x4 tr16(const _Float16* p) {
-  s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
-  return __builtin_bit_cast(f16x4, t);
+__device__ __forceinline__ s16x4_t tr16raw(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
 }
 
-__device__ __forceinline__ f16x8 cvt8(u32x4 raw) {
-  const u16x8 b = __builtin_bit_cast(u16x8, raw);
-  f16x8 h;
+// Valid context length of sequence b (0 for a length outside [1, S_max]).
+__device__ __forceinline__ int dec_len(const int32_t* __restrict__ ctx_len, int b, int S_max) {
+  const int c = ctx_len[b];
+  return (c >= 1 && c <= S_max) ? c : 0;
+}
+
+// Wave-uniform value into scalar registers (the caller guarantees uniformity).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ long long uni(long long x) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)(x & 0xffffffffll));
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)x >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+__device__ __forceinline__ long long wave_sum_ll(long long x) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) h[e] = bf16_bits_to_f16(b[e]);
-  return h;
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
 }
 
+// Start of the balanced range of workgroup w of P, in keys of the flattened space.
+__device__ __forceinline__ long long bal_lo(long long w, long long W, int P) { return w * W / P; }
+
+// Total keys of the flattened space: Hkv * sum of valid lengths (every lane).
+__device__ long long bal_total(const int32_t* __restrict__ ctx_len, int B, int Hkv, int S_max) {
+  const int lane = threadIdx.x & 63;
+  long long s = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    s += wave_sum_ll(b < B ? dec_len(ctx_len, b, S_max) : 0);
+  }
+  return s * Hkv;
+}
+
+// One workgroup's pass over keys [k_begin, k_end) of (b, hk) for the G heads
+// hq0 .. hq0+G-1; writes record hh at rec + hh * rec_stride:
+//   [m (log2 units), l, e, C, O[D], U[D]].
 template <int D, int G>
-__global__ __launch_bounds__(DEC_THREADS, 2) void decode16_partial_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ rho, const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, const int32_t* __restrict__ ctx_len, float* __restrict__ part,
-    int Hq, int Hkv, int S_max, int chunk, int nsplit, int hoff, float scale_log2) {
-  constexpr int NS = D / 32;   // 32-deep score steps
-  constexpr int ND = D / 16;   // 16-row d tiles of the value / Kbar accumulators
-  constexpr int REC = 3 * D + 4;
+__device__ __forceinline__ void dec16_range(Dec16Smem<D>& sm, const uint16_t* __restrict__ q,
+                                            const uint16_t* __restrict__ rho,
+                                            const uint16_t* __restrict__ kc,
+                                            const uint16_t* __restrict__ vc, int b, int hk, int hq0,
+                                            int Hq, int Hkv, int S_max, int k_begin, int k_end,
+                                            float scale_log2, float* __restrict__ rec, size_t rec_stride) {
+  constexpr int NS = D / 32;  // 32-deep score steps
+  constexpr int ND = D / 16;  // 16-row d tiles of the value accumulators
   using SM = Dec16Smem<D>;
-  __shared__ SM sm;
-
-  const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-  const int ctx = ctx_len[b];
-  if (ctx < 1 || ctx > S_max) return;  // the merge writes NaN for this sequence
-  const int k_begin = split * chunk;
-  if (k_begin >= ctx) return;          // the merge reads only splits below ctx
-  const int k_end = min(ctx, k_begin + chunk);
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
-  const int hq0 = hk * (Hq / Hkv) + hoff;  // first query head of these columns
 
-  // B operand of the score MFMAs: column c -> q (even) / rho (odd) of head hq0 + c/2
-  bf16x8_t bop[NS];
-  {
-    const uint16_t* src = (c & 1) ? rho : q;
-    const size_t row = ((size_t)b * Hq + hq0 + (c >> 1)) * D;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (c < 2 * G) raw = *reinterpret_cast<const u32x4*>(src + row + 32 * s + 8 * g);
-      bop[s] = __builtin_bit_cast(bf16x8_t, raw);
+  // B operand of the score MFMAs, staged once in LDS: column cc holds q (even)
+  // or rho (odd) of head hq0 + cc/2 (zero for unused columns)
+  for (int i = threadIdx.x; i < 16 * D / 8; i += DEC_THREADS) {
+    const int cc = i / (D / 8), d0 = (i % (D / 8)) * 8;
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (cc < 2 * G) {
+      const uint16_t* src = (cc & 1) ? rho : q;
+      raw = *reinterpret_cast<const u32x4*>(src + ((size_t)b * Hq + hq0 + (cc >> 1)) * D + d0);
     }
+    *reinterpret_cast<u32x4*>(&sm.bq[cc * D + d0]) = raw;
   }
+  __syncthreads();
   const uint16_t* kbase = kc + ((size_t)(b * Hkv + hk) * S_max) * D;
   const uint16_t* vbase = vc + ((size_t)(b * Hkv + hk) * S_max) * D;
-  _Float16* kt = sm.tiles[wave][0];
-  _Float16* vt = sm.tiles[wave][1];
+  uint16_t* vt = sm.tiles[wave];
 
-  f32x4 ou[ND], kb[ND];
+  f32x4 ou[ND];
 #pragma unroll
-  for (int i = 0; i < ND; ++i) {
-    ou[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    kb[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  }
+  for (int i = 0; i < ND; ++i) ou[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_part = 0.f, e_part = 0.f;
   const bool used = c < 2 * G;
   const bool odd = c & 1;
 
   // raw bf16 K and V of one sub-tile: [key tile t][d step s]
-  u32x4 kr[2][NS], vr[2][NS];
-  auto load_sub = [&](int key0) {
+  u32x4 kr[DEC_NSET][2][NS], vr[DEC_NSET][2][NS];
+  auto load_sub = [&](u32x4 (&kx)[2][NS], u32x4 (&vx)[2][NS], int key0) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       // rows past k_end load row k_end-1 (valid, finite); they are masked below
@@ -365,37 +382,33 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_partial_kernel(
       const uint16_t* vp = vbase + (size_t)key * D + 8 * g;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        kr[t][s] = *reinterpret_cast<const u32x4*>(kp + 32 * s);
-        vr[t][s] = *reinterpret_cast<const u32x4*>(vp + 32 * s);
+        kx[t][s] = *reinterpret_cast<const u32x4*>(kp + 32 * s);
+        vx[t][s] = *reinterpret_cast<const u32x4*>(vp + 32 * s);
       }
     }
   };
 
-  int key0 = k_begin + DEC_SUB * wave;
-  if (key0 < k_end) load_sub(key0);
-  for (; key0 < k_end; key0 += DEC_GROUP_KEYS) {
-    // scores of the two 16-key tiles
+  auto process = [&](u32x4 (&kx)[2][NS], u32x4 (&vx)[2][NS], int key0) {
     f32x4 sacc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       sacc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[t][s]), bop[s],
-                                                          sacc[t], 0, 0, 0);
+        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, kx[t][s]),
+            *reinterpret_cast<const bf16x8_t*>(&sm.bq[c * D + 32 * s + 8 * g]), sacc[t], 0, 0, 0);
     }
-    // stage K and V rows (fp16) in this wave's LDS tiles
+    // stage the raw V rows; the loaded registers feed only this write and the
+    // score MFMAs
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int off = (16 * t + c) * SM::LD + 32 * s + 8 * g;
-        *reinterpret_cast<f16x8*>(kt + off) = cvt8(kr[t][s]);
-        *reinterpret_cast<f16x8*>(vt + off) = cvt8(vr[t][s]);
-      }
-    // next sub-tile's loads go out now (registers are free again)
-    const int next = key0 + DEC_GROUP_KEYS;
-    if (next < k_end) load_sub(next);
+      for (int s = 0; s < NS; ++s)
+        *reinterpret_cast<u32x4*>(vt + (16 * t + c) * SM::LD + 32 * s + 8 * g) = vx[t][s];
+    // this set's next loads, unconditionally: past the end the rows clamp to
+    // k_end-1, so every sub-tile issues the same loads and the waits stay exact
+    load_sub(kx, vx, key0 + DEC_NSET * DEC_GROUP_KEYS);
     wave_lds_sync();
 
     // softmax: even columns hold scores, odd columns r
@@ -422,10 +435,7 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_partial_kernel(
 #pragma unroll
       for (int i = 0; i < ND; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          ou[i][j] *= alpha;
-          kb[i][j] *= alpha;
-        }
+        for (int j = 0; j < 4; ++j) ou[i][j] *= alpha;
       m_run = m_new;
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
@@ -443,31 +453,41 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_partial_kernel(
     l_part += lsum;
     e_part += esum;
 
-    // value and Kbar MFMAs: A operands V^T and K^T from the transpose reads;
-    // element e of group g is key 16*(e/4) + 4*g + e%4, matching pop
+    // value MFMAs: A operand V^T from the transpose reads; element e of
+    // group g is key 16*(e/4) + 4*g + e%4, matching pop
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
       const int off = (4 * g + (c >> 2)) * SM::LD + 16 * dt + 4 * (c & 3);
-      const f16x4 v0 = tr16(vt + off), v1 = tr16(vt + off + 16 * SM::LD);
-      const f16x4 k0 = tr16(kt + off), k1 = tr16(kt + off + 16 * SM::LD);
-      f16x8 av, ak;
+      const s16x4_t v0 = tr16raw(vt + off), v1 = tr16raw(vt + off + 16 * SM::LD);
+      f16x8 av;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        av[e] = v0[e];
-        av[4 + e] = v1[e];
-        ak[e] = k0[e];
-        ak[4 + e] = k1[e];
+        av[e] = bf16_bits_to_f16((uint16_t)v0[e]);
+        av[4 + e] = bf16_bits_to_f16((uint16_t)v1[e]);
       }
       ou[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pop, ou[dt], 0, 0, 0);
-      kb[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ak, pop, kb[dt], 0, 0, 0);
     }
     wave_lds_sync();
+  };
+
+  // Sub-tiles past k_end (at most DEC_NSET-1 per wave, at the end) are
+  // processed too: every key is masked (p = 0), so they add nothing.
+  int key0 = k_begin + DEC_SUB * wave;
+#pragma unroll
+  for (int i = 0; i < DEC_NSET; ++i) {
+    // issue the sets oldest-first so each wait in the loop covers one set only
+    load_sub(kr[i], vr[i], key0 + i * DEC_GROUP_KEYS);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (; key0 < k_end; key0 += DEC_NSET * DEC_GROUP_KEYS) {
+#pragma unroll
+    for (int i = 0; i < DEC_NSET; ++i) process(kr[i], vr[i], key0 + i * DEC_GROUP_KEYS);
   }
 
   // ---- merge the four waves' states through LDS ----
   __syncthreads();
   if (g == 0) sm.mw[wave][c] = m_run;
-  for (int i = threadIdx.x; i < 2 * 16 * SM::MLD; i += DEC_THREADS) (&sm.merge[0][0])[i] = 0.f;
+  for (int i = threadIdx.x; i < 16 * SM::MLD; i += DEC_THREADS) sm.merge[i] = 0.f;
   if (threadIdx.x < 16) {
     sm.lsum[threadIdx.x] = 0.f;
     sm.esum[threadIdx.x] = 0.f;
@@ -491,27 +511,106 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_partial_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d = 16 * dt + 4 * g + j;
-      atomicAdd(&sm.merge[0][c * SM::MLD + d], ou[dt][j] * sc);
-      atomicAdd(&sm.merge[1][c * SM::MLD + d], kb[dt][j] * sc);
+      atomicAdd(&sm.merge[c * SM::MLD + d], ou[dt][j] * sc);
     }
   __syncthreads();
 
-  // record of head g: [m, l, e, 0, O[D], U[D], Kbar[D]]  (m in log2 units)
   for (int hh = 0; hh < G; ++hh) {
-    float* rec = part + (((size_t)b * Hq + hq0 + hh) * nsplit + split) * REC;
+    float* r = rec + hh * rec_stride;
     const int c0 = 2 * hh;
     if (threadIdx.x == 0) {
       float M0 = -INFINITY;
       for (int w = 0; w < DEC_WAVES; ++w) M0 = fmaxf(M0, sm.mw[w][c0]);
-      rec[0] = M0;
-      rec[1] = sm.lsum[c0];
-      rec[2] = sm.esum[c0];
-      rec[3] = 0.f;
+      r[0] = M0;
+      r[1] = sm.lsum[c0];
+      r[2] = sm.esum[c0];
+      r[3] = sm.lsum[c0 + 1];
     }
     for (int d = threadIdx.x; d < D; d += DEC_THREADS) {
-      rec[4 + d] = sm.merge[0][c0 * SM::MLD + d];
-      rec[4 + D + d] = sm.merge[0][(c0 + 1) * SM::MLD + d];
-      rec[4 + 2 * D + d] = sm.merge[1][c0 * SM::MLD + d];
+      r[4 + d] = sm.merge[c0 * SM::MLD + d];
+      r[4 + D + d] = sm.merge[(c0 + 1) * SM::MLD + d];
+    }
+  }
+  __syncthreads();  // the next range reuses the LDS tiles that alias the merge buffer
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(DEC_THREADS, 2) void decode16_chunk_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ rho, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ ctx_len, float* __restrict__ part,
+    int Hq, int Hkv, int S_max, int chunk, int nsplit, int hoff, float scale_log2) {
+  constexpr int REC = 2 * D + 4;
+  __shared__ Dec16Smem<D> sm;
+  const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int ctx = dec_len(ctx_len, b, S_max);
+  const int k_begin = split * chunk;
+  if (k_begin >= ctx) return;  // the merge reads only splits below ctx (none if ctx is invalid)
+  const int k_end = min(ctx, k_begin + chunk);
+  const int hq0 = hk * (Hq / Hkv) + hoff;
+  float* rec = part + (((size_t)b * Hq + hq0) * nsplit + split) * REC;
+  dec16_range<D, G>(sm, q, rho, kc, vc, b, hk, hq0, Hq, Hkv, S_max, k_begin, k_end, scale_log2, rec,
+                    (size_t)nsplit * REC);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(DEC_THREADS, 2) void decode16_balanced_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ rho, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ ctx_len, float* __restrict__ part,
+    int B, int Hq, int Hkv, int S_max, int hoff, float scale_log2) {
+  constexpr int REC = 2 * D + 4;
+  __shared__ Dec16Smem<D> sm;
+  const int lane = threadIdx.x & 63;
+  const int Gfull = Hq / Hkv;
+  const int P = gridDim.x;
+  const long long W = uni(bal_total(ctx_len, B, Hkv, S_max));
+  const long long lo = bal_lo(blockIdx.x, W, P), hi = bal_lo(blockIdx.x + 1, W, P);
+  if (lo >= hi) return;
+
+  // first sequence whose segments reach past lo: Hkv * (keys before b + len b) > lo
+  int b = 0;
+  long long before = 0;  // Hkv * (valid keys of sequences before b)
+  {
+    long long base = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int bb = b0 + lane;
+      const long long len = bb < B ? dec_len(ctx_len, bb, S_max) : 0;
+      long long incl = len;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const long long t = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += t;
+      }
+      const unsigned long long hit = __ballot(bb < B && (base + incl) * Hkv > lo);
+      if (hit) {
+        const int first = __ffsll(hit) - 1;
+        b = b0 + first;
+        before = __shfl(base + incl - len, first, 64) * Hkv;
+        break;
+      }
+      base += __shfl(incl, 63, 64);
+    }
+  }
+  b = uni(b);
+  before = uni(before);
+  int len = uni(dec_len(ctx_len, b, S_max));
+  int hk = (int)((lo - before) / len);
+  int key = (int)((lo - before) % len);
+  long long pos = lo;
+  while (true) {
+    const int k_end = (int)min((long long)len, key + (hi - pos));
+    const int hq0 = hk * Gfull + hoff;
+    const long long slot = (long long)blockIdx.x + (long long)b * Hkv + hk;
+    float* rec = part + ((size_t)slot * Gfull + hoff) * REC;
+    dec16_range<D, G>(sm, q, rho, kc, vc, b, hk, hq0, Hq, Hkv, S_max, key, k_end, scale_log2, rec, REC);
+    pos += k_end - key;
+    if (pos >= hi) break;
+    key = 0;
+    if (++hk == Hkv) {
+      hk = 0;
+      do {
+        ++b;
+        len = uni(dec_len(ctx_len, b, S_max));
+      } while (len == 0);  // pos < hi <= W guarantees a later non-empty sequence
     }
   }
 }
@@ -520,58 +619,162 @@ template <int D, int G>
 hipError_t launch_partial16(const void* q, const void* rho, const void* kc, const void* vc,
                             const int32_t* ctx_len, float* part, int B, int Hq, int Hkv, int S_max,
                             int chunk, int nsplit, int hoff, float scale, hipStream_t stream) {
-  dim3 grid(nsplit, Hkv, B);
-  hipLaunchKernelGGL((decode16_partial_kernel<D, G>), grid, dim3(DEC_THREADS), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)rho, (const uint16_t*)kc, (const uint16_t*)vc,
-                     ctx_len, part, Hq, Hkv, S_max, chunk, nsplit, hoff, scale * kLog2e);
+  if (chunk <= 0) {
+    hipLaunchKernelGGL((decode16_balanced_kernel<D, G>), dim3(nsplit), dim3(DEC_THREADS), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)rho, (const uint16_t*)kc, (const uint16_t*)vc,
+                       ctx_len, part, B, Hq, Hkv, S_max, hoff, scale * kLog2e);
+  } else {
+    dim3 grid(nsplit, Hkv, B);
+    hipLaunchKernelGGL((decode16_chunk_kernel<D, G>), grid, dim3(DEC_THREADS), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)rho, (const uint16_t*)kc, (const uint16_t*)vc,
+                       ctx_len, part, Hq, Hkv, S_max, chunk, nsplit, hoff, scale * kLog2e);
+  }
   return hipGetLastError();
 }
 
-template <class Pol, int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict__ part,
-                                                         const typename Pol::in_t* __restrict__ rho,
-                                                         const int32_t* __restrict__ ctx_len,
-                                                         float* __restrict__ o, float* __restrict__ lse,
-                                                         int Hq, int S_max, int chunk, int nsplit) {
-  constexpr int REC = 3 * D + 4;
-  __shared__ float red[D / 64];
+// Merge: rescale a head's n records to their common max M and finish
+//   o = (O/l)(1 + C/l) - U/l,   LSE = M + ln e   (natural log).
+// Record i sits at rec0 + i * stride; a record with valid(i) false was never
+// written and is skipped.  The block (one thread per output element) reads the
+// record headers in parallel and then streams O and U with independent loads.
+template <int D, class Valid>
+__device__ __forceinline__ void merge_records(const float* __restrict__ rec0, size_t stride, int n,
+                                              Valid valid, float* __restrict__ orow,
+                                              float* __restrict__ lse_out) {
+  constexpr int NW = D / 64;
+  __shared__ float red[4][NW];
+  __shared__ float scale_s[D];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  auto block_reduce = [&](float x, int slot, bool is_max) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float y = __shfl_xor(x, off, 64);
+      x = is_max ? fmaxf(x, y) : x + y;
+    }
+    if (lane == 0) red[slot][wave] = x;
+    __syncthreads();
+    float r = red[slot][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) r = is_max ? fmaxf(r, red[slot][w]) : r + red[slot][w];
+    return r;
+  };
+  float M = -INFINITY;
+  for (int i = t; i < n; i += D)
+    if (valid(i)) M = fmaxf(M, rec0[(size_t)i * stride]);
+  M = block_reduce(M, 0, true);
+  float l = 0.f, e = 0.f, C = 0.f, O = 0.f, U = 0.f;
+  for (int base = 0; base < n; base += D) {
+    const int i = base + t;
+    float a = 0.f;
+    if (i < n && valid(i)) {
+      const float* r = rec0 + (size_t)i * stride;
+      a = fast_exp2(r[0] - M);
+      l += a * r[1];
+      e += a * r[2];
+      C += a * r[3];
+    }
+    __syncthreads();  // previous batch's scale_s reads are done
+    scale_s[t] = a;
+    __syncthreads();
+    const int cnt = min(D, n - base);
+#pragma unroll 4
+    for (int k = 0; k < cnt; ++k) {
+      const float ak = scale_s[k];
+      if (ak != 0.f) {
+        const float* r = rec0 + (size_t)(base + k) * stride;
+        O += ak * r[4 + t];
+        U += ak * r[4 + D + t];
+      }
+    }
+  }
+  l = block_reduce(l, 1, false);
+  e = block_reduce(e, 2, false);
+  C = block_reduce(C, 3, false);
+  const float inv = 1.f / l;
+  orow[t] = O * inv * (1.f + C * inv) - U * inv;
+  if (lse_out && t == 0) *lse_out = (M + __log2f(e)) * kLn2;
+}
+
+__device__ __forceinline__ void write_nan_row(float* orow, float* lse_out, int t) {
+  orow[t] = __builtin_nanf("");
+  if (lse_out && t == 0) *lse_out = __builtin_nanf("");
+}
+
+// Chunked schedule: the records of (b, h) are splits 0 .. ceil(ctx/chunk)-1.
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_chunk_kernel(const float* __restrict__ part,
+                                                               const int32_t* __restrict__ ctx_len,
+                                                               float* __restrict__ o, float* __restrict__ lse,
+                                                               int Hq, int S_max, int chunk, int nsplit) {
+  constexpr int REC = 2 * D + 4;
   const int bh = blockIdx.x;
-  const int b = bh / Hq;
   const int t = threadIdx.x;
-  const int ctx = ctx_len[b];
+  const int ctx = dec_len(ctx_len, bh / Hq, S_max);
   float* orow = o + (size_t)bh * D;
-  if (ctx < 1 || ctx > S_max) {
-    orow[t] = __builtin_nanf("");
-    if (lse && t == 0) lse[bh] = __builtin_nanf("");
+  float* lse_out = lse ? lse + bh : nullptr;
+  if (ctx == 0) {
+    write_nan_row(orow, lse_out, t);
     return;
   }
   const int n = (ctx + chunk - 1) / chunk;
-  const float* recs = part + (size_t)bh * nsplit * REC;
-  float M = -INFINITY;
-  for (int s = 0; s < n; ++s) M = fmaxf(M, recs[(size_t)s * REC]);
-  float l = 0.f, le = 0.f, O = 0.f, U = 0.f, Kb = 0.f;
-  for (int s = 0; s < n; ++s) {
-    const float* r = recs + (size_t)s * REC;
-    const float a = fast_exp2(r[0] - M);
-    l += a * r[1];
-    le += a * r[2];
-    O += a * r[4 + t];
-    U += a * r[4 + D + t];
-    Kb += a * r[4 + 2 * D + t];
+  merge_records<D>(part + (size_t)bh * nsplit * REC, REC, n, [](int) { return true; }, orow, lse_out);
+}
+
+// Balanced schedule: the records of (b, h) sit at slots w + s for the
+// workgroups w whose range meets segment s = b * Hkv + h / G.
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_balanced_kernel(const float* __restrict__ part,
+                                                                  const int32_t* __restrict__ ctx_len,
+                                                                  float* __restrict__ o, float* __restrict__ lse,
+                                                                  int B, int Hq, int Hkv, int S_max, int P) {
+  constexpr int REC = 2 * D + 4;
+  __shared__ long long red_ll[2][D / 64];
+  const int bh = blockIdx.x;
+  const int b = bh / Hq, h = bh % Hq;
+  const int Gfull = Hq / Hkv;
+  const int hk = h / Gfull;
+  const int t = threadIdx.x;
+  const int len = dec_len(ctx_len, b, S_max);
+  float* orow = o + (size_t)bh * D;
+  float* lse_out = lse ? lse + bh : nullptr;
+  if (len == 0) {
+    write_nan_row(orow, lse_out, t);
+    return;
   }
-  // c = (Kbar . rho) / l
-  float x = Kb * Pol::to_f32(rho[(size_t)bh * D + t]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  if ((t & 63) == 0) red[t >> 6] = x;
+  // total valid keys and keys before b, block-wide
+  long long tot = 0, pre = 0;
+  for (int bb = t; bb < B; bb += D) {
+    const int l = dec_len(ctx_len, bb, S_max);
+    tot += l;
+    if (bb < b) pre += l;
+  }
+  tot = wave_sum_ll(tot);
+  pre = wave_sum_ll(pre);
+  if ((t & 63) == 0) {
+    red_ll[0][t >> 6] = tot;
+    red_ll[1][t >> 6] = pre;
+  }
   __syncthreads();
-  float dot = 0.f;
+  tot = 0;
+  pre = 0;
 #pragma unroll
-  for (int w = 0; w < D / 64; ++w) dot += red[w];
-  const float inv = 1.f / l;
-  const float c = dot * inv;
-  orow[t] = O * inv * (1.f + c) - U * inv;
-  if (lse && t == 0) lse[bh] = (M + __log2f(le)) * kLn2;
+  for (int w = 0; w < D / 64; ++w) {
+    tot += red_ll[0][w];
+    pre += red_ll[1][w];
+  }
+  const long long W = tot * Hkv;
+  const long long start = pre * Hkv + (long long)hk * len, end = start + len;
+  // workgroup whose range holds `start`
+  long long w = start * P / W;
+  while (w + 1 < P && bal_lo(w + 1, W, P) <= start) ++w;
+  while (w > 0 && bal_lo(w, W, P) > start) --w;
+  const long long seg = (long long)b * Hkv + hk;
+  // workgroups w .. w+n-1 meet the segment; one with an empty range wrote no record
+  int n = 0;
+  while (w + n < P && bal_lo(w + n, W, P) < end) ++n;
+  const float* rec0 = part + ((size_t)(w + seg) * Gfull + (h % Gfull)) * REC;
+  merge_records<D>(rec0, (size_t)Gfull * REC, n,
+                   [&](int i) { return bal_lo(w + i, W, P) < bal_lo(w + i + 1, W, P); }, orow, lse_out);
 }
 
 template <class Pol, int D, int G>
@@ -591,7 +794,6 @@ hipError_t launch_decode_t(const void* q, const void* rho, const void* kc, const
                            const int32_t* ctx_len, float* o, float* lse, int B, int Hq, int Hkv,
                            int S_max, float scale, int chunk, int nsplit, float* part,
                            hipStream_t stream) {
-  using in_t = typename Pol::in_t;
   const int G = Hq / Hkv;
   hipError_t e;
   if constexpr (sizeof(typename Pol::in_t) == 2) {
@@ -608,21 +810,27 @@ hipError_t launch_decode_t(const void* q, const void* rho, const void* kc, const
         break;
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<Pol, D>), dim3(B * Hq), dim3(D), 0, stream, part,
-                       (const in_t*)rho, ctx_len, o, lse, Hq, S_max, chunk, nsplit);
+    if (chunk <= 0)
+      hipLaunchKernelGGL((decode_merge_balanced_kernel<D>), dim3(B * Hq), dim3(D), 0, stream, part,
+                         ctx_len, o, lse, B, Hq, Hkv, S_max, nsplit);
+    else
+      hipLaunchKernelGGL((decode_merge_chunk_kernel<D>), dim3(B * Hq), dim3(D), 0, stream, part,
+                         ctx_len, o, lse, Hq, S_max, chunk, nsplit);
+    return hipGetLastError();
+  } else {
+    // fp32: the generic 32-column kernel (chunked schedule only)
+    switch (G) {
+      case 1: e = launch_partial<Pol, D, 1>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
+      case 2: e = launch_partial<Pol, D, 2>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
+      case 4: e = launch_partial<Pol, D, 4>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
+      case 8: e = launch_partial<Pol, D, 8>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
+      default: e = launch_partial<Pol, D, 16>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
+    }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_merge_chunk_kernel<D>), dim3(B * Hq), dim3(D), 0, stream, part, ctx_len,
+                       o, lse, Hq, S_max, chunk, nsplit);
     return hipGetLastError();
   }
-  switch (G) {
-    case 1: e = launch_partial<Pol, D, 1>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
-    case 2: e = launch_partial<Pol, D, 2>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
-    case 4: e = launch_partial<Pol, D, 4>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
-    case 8: e = launch_partial<Pol, D, 8>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
-    default: e = launch_partial<Pol, D, 16>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
-  }
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<Pol, D>), dim3(B * Hq), dim3(D), 0, stream, part,
-                     (const in_t*)rho, ctx_len, o, lse, Hq, S_max, chunk, nsplit);
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -646,12 +854,34 @@ int decode_chunk_keys(int S_max, int num_splits) {
   return c;
 }
 
-size_t decode_record_floats(int d) { return 3 * (size_t)d + 4; }
+size_t decode_record_floats(int d) { return 2 * (size_t)d + 4; }
+
+// Workgroups of the balanced schedule: two per compute unit, fewer when the
+// cache holds under ~1024 keys per workgroup.
+int decode_balanced_ctas(int B, int Hkv, int S_max) {
+  const long long keys = (long long)B * Hkv * S_max;
+  long long p = (keys + 1023) / 1024;
+  if (p > DEC_BAL_CTAS) p = DEC_BAL_CTAS;
+  return p < 1 ? 1 : (int)p;
+}
+
+// Record slots of the balanced schedule: one per (workgroup, segment) piece,
+// at most P + B * Hkv.
+size_t decode_balanced_records(int B, int Hq, int Hkv, int S_max) {
+  return ((size_t)decode_balanced_ctas(B, Hkv, S_max) + (size_t)B * Hkv) * (size_t)(Hq / Hkv);
+}
 
 hipError_t launch_decode(int dtype, const void* q, const void* rho, const void* k_cache,
                          const void* v_cache, const int32_t* ctx_len, float* o, float* lse, int B,
                          int Hq, int Hkv, int S_max, int d, float scale, int num_splits,
                          float* partials, hipStream_t stream) {
+  if (dtype == PLX_BF16 && num_splits == 0) {
+    // balanced schedule (chunk 0); nsplit carries the workgroup count
+    const int P = decode_balanced_ctas(B, Hkv, S_max);
+    if (d == 64)
+      return launch_decode_t<PolBF16, 64>(q, rho, k_cache, v_cache, ctx_len, o, lse, B, Hq, Hkv, S_max, scale, 0, P, partials, stream);
+    return launch_decode_t<PolBF16, 128>(q, rho, k_cache, v_cache, ctx_len, o, lse, B, Hq, Hkv, S_max, scale, 0, P, partials, stream);
+  }
   int ns = num_splits > 0 ? num_splits : decode_auto_splits(B, Hkv, S_max);
   if (ns > S_max) ns = S_max;
   const int chunk = decode_chunk_keys(S_max, ns);

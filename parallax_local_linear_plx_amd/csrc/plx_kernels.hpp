@@ -18,6 +18,8 @@ hipError_t launch_fwd(int dtype, const void* q, const void* k, const void* v, co
 int decode_auto_splits(int B, int Hkv, int S_max);
 int decode_chunk_keys(int S_max, int num_splits);
 size_t decode_record_floats(int d);
+int decode_balanced_ctas(int B, int Hkv, int S_max);
+size_t decode_balanced_records(int B, int Hq, int Hkv, int S_max);
 hipError_t launch_decode(int dtype, const void* q, const void* rho, const void* k_cache,
                          const void* v_cache, const int32_t* ctx_len, float* o, float* lse, int B,
                          int Hq, int Hkv, int S_max, int d, float scale, int num_splits,

@@ -93,7 +93,7 @@ def test_decode_workspace_size_is_consistent():
     n0 = binding.decode_workspace_size(64, 16, 8, 8192, 128, 0)
     assert n0 > 0 and n0 % 16 == 0
     n4 = binding.decode_workspace_size(64, 16, 8, 8192, 128, 4)
-    rec = 3 * 128 + 4
+    rec = 2 * 128 + 4
     assert n4 == 64 * 16 * 4 * rec * 4
     assert binding.decode_workspace_size(0, 16, 8, 8192, 128, 0) == 0
     # exactly the reported size is accepted by validation (up to the launch)

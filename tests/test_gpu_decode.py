@@ -98,6 +98,34 @@ def test_mapping_probe_and_invalid_lengths(gpu_lib):
         assert np.all(np.isnan(o[b])) and np.all(np.isnan(got["lse"][b]))
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(16, 8), (32, 2)])
+def test_bf16_balanced_schedule_many_short_sequences(gpu_lib, Hq, Hkv):
+    """Automatic schedule over many short ragged sequences: workgroup ranges
+    span several (b, kv head) segments.  Valid sequences match the oracle and
+    the explicit-split path; lengths outside [1, S_max] give NaN rows."""
+    import torch
+
+    B, d, S = 40, 128, 300
+    say(f"case decode bf16 balanced B{B} Hq{Hq} Hkv{Hkv} ctx U{{1..{S}}} + invalid lengths")
+    wl = inputs.make_decode(B, Hq, Hkv, d, 0, S_max=S, dtype="bf16", seed=85, ctx_range=(1, S))
+    t = _dev(wl)
+    ctx = wl.ctx_len.copy()
+    ctx[[3, 17]] = [0, S + 1]  # invalid: those rows must be NaN
+    t["ctx"] = torch.from_numpy(ctx).cuda()
+    got = _run(wl, 0, t)
+    split = _run(wl, 3, t)
+    valid = [b for b in range(B) if 1 <= ctx[b] <= S]
+    for b in (3, 17):
+        assert np.all(np.isnan(got["o"][b])) and np.all(np.isnan(got["lse"][b]))
+    heads = [(b, h) for b in valid for h in range(Hq)]
+    ref = _oracle(wl, heads)
+    o = np.array([got["o"][b, h] for b, h in heads])
+    check_bf16(o, ref["o"], "o")
+    assert np.max(np.abs(np.array([got["lse"][b, h] for b, h in heads]) - ref["lse"])) <= LSE_ABS
+    o_split = np.array([split["o"][b, h] for b, h in heads])
+    assert np.max(np.abs(o - o_split)) < 1e-3
+
+
 def test_decode_matches_prefill_last_row(gpu_lib):
     """Decode over the first t cache rows equals the prefill output at row t-1
     (both on the GPU, both checked against the oracle)."""
