@@ -313,7 +313,7 @@ def main():
                                   "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                   "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4),
                                   "traffic": measured_traffic("prefill"),
-                                  "kernel": "fwd_kernel<PolBF16,128>",
+                                  "kernel": "fwd16_kernel<128,8>",
                                   "algorithmic_flops_per_launch": p["flops"]}})
     else:
         line.update({"value": None, "unit": "TFLOP/s", "ms_per_step": None, "config": {"workload": args.only}})

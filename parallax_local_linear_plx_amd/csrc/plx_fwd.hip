@@ -16,19 +16,12 @@
 // and RK are formed by the same matrix instructions; here the stacked
 // [Q; rho] K^T is two MFMA chains sharing every K operand.
 //
-// Work split: a workgroup (4 waves) owns 128 query rows of one (b, h);
-// each wave owns 32 rows, with its Q and rho rows held as MFMA B operands
-// for the whole pass.  Keys stream in tiles of 64 through double-buffered LDS:
-//   K tile  row-major [64][D + pad]   A operand of S^T = K Q^T and R^T = K rho^T
-//   V tile  bf16 path: row-major fp16 [64][D + 32], read transposed by
-//           ds_read_b64_tr_b16 as the A operand of O^T = V^T P^T, U^T = V^T (P.R)^T;
-//           fp32 path: stored transposed [D][64 + 4].
-// Pipeline per 64-key iteration j (one barrier): global loads of K(j+2) and
-// V(j+1) are issued first into registers; for each 32-key sub-tile t the score
-// MFMAs of t+1 are issued before the softmax (VALU) and value MFMAs of t, so
-// the two overlap; last, the prefetched registers go to the free LDS buffers.
-// (The fp32 path, whose Q and rho operands alone take 128 registers at
-// d = 128, computes each sub-tile's scores just before its softmax.)
+// Two kernels share this file:
+//   * fwd16_kernel (bf16 inputs): 16x16x32 MFMA tiles, 16 query rows per
+//     wave, 8 waves per workgroup, two waves per SIMD (described below);
+//   * fwd_kernel (fp32 inputs, the exact-parity path): 32x32x2 fp32 MFMAs,
+//     4 waves of 32 query rows; K rows and transposed V through double-
+//     buffered LDS, one sub-tile at a time (scores, softmax, value MFMAs).
 #include "plx_common.hpp"
 #include "plx_kernels.hpp"
 
@@ -39,6 +32,7 @@ namespace {
 constexpr int FWD_BR = 128;
 constexpr int FWD_BC = 64;
 constexpr int FWD_THREADS = 256;
+constexpr int FWD16_WAVES = 8;  // waves per workgroup of the bf16 kernel
 // Lazy-rescale threshold (log2 units): p stays <= 16, so the fp16 operand
 // p * r overflows only for |r| = |rho . k| > 4094.
 constexpr float kRescaleLog2 = 4.f;
@@ -320,74 +314,6 @@ __device__ __forceinline__ void softmax_pv_body(FwdState<Pol, D>& S, const FwdSm
   }
 }
 
-// One pipelined sub-tile step of the bf16 path, as a fixed instruction order
-// (sched_barrier sections):
-//   sections 0..NS-1: one score MFMA pair (S, R) of the NEXT sub-tile, with
-//     its K operand read two sections ahead, interleaved with the exp / p.r
-//     work of 16/NS elements of the CURRENT sub-tile;
-//   then the fp16 packing and row sums of the current sub-tile;
-//   then its value MFMAs (O, U), each V operand read one step ahead.
-// The next scores are computed unconditionally (for the last sub-tile they
-// read a valid but stale LDS buffer and are discarded).
-template <int D>
-__device__ __forceinline__ void subtile_step_bf16(FwdState<PolBF16, D>& S,
-                                                  const FwdSmem<PolBF16, D>& sm, int kbuf_next,
-                                                  int st_next, int vbuf, int st_cur, int col,
-                                                  int half, int lane, float scale_log2, float m_use,
-                                                  const bf16x8* qop, const bf16x8* rop,
-                                                  const f32x16& sc, const f32x16& rc, f32x16& sn,
-                                                  f32x16& rn) {
-  using SM = FwdSmem<PolBF16, D>;
-  constexpr int NS = D / 16;    // score MFMA steps
-  constexpr int ND = D / 32;    // value d sub-tiles
-  constexpr int EPS = 16 / NS;  // softmax elements per section
-  const uint16_t* krow = &sm.k[kbuf_next][(32 * st_next + col) * SM::KLD + 8 * half];
-  bf16x8 kb[NS];
-  f16x8 pop[2], prop[2];
-  float lsum = 0.f, csum = 0.f;
-  kb[0] = load_sop<PolBF16>(krow);
-  kb[1] = load_sop<PolBF16>(krow + 16);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    if (i + 2 < NS) kb[i + 2] = load_sop<PolBF16>(krow + 16 * (i + 2));
-    sn = PolBF16::mma_s(kb[i], qop[i], i == 0 ? zero16() : sn);
-    rn = PolBF16::mma_s(kb[i], rop[i], i == 0 ? zero16() : rn);
-    // exp / p.r of EPS elements, packed to fp16 pairs as they are produced
-#pragma unroll
-    for (int e = 0; e < EPS; e += 2) {
-      const int a = EPS * i + e;
-      const float p0 = fast_exp2(__builtin_fmaf(sc[a], scale_log2, -m_use));
-      const float p1 = fast_exp2(__builtin_fmaf(sc[a + 1], scale_log2, -m_use));
-      S.e_part += p0 + p1;
-      const f16x2 ph = {(_Float16)p0, (_Float16)p1};
-      const f16x2 rh = {(_Float16)(p0 * rc[a]), (_Float16)(p1 * rc[a + 1])};
-      const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
-      lsum = __builtin_amdgcn_fdot2(ph, one, lsum, false);
-      csum = __builtin_amdgcn_fdot2(rh, one, csum, false);
-      pop[a >> 3][a & 7] = ph[0];
-      pop[a >> 3][(a & 7) + 1] = ph[1];
-      prop[a >> 3][a & 7] = rh[0];
-      prop[a >> 3][(a & 7) + 1] = rh[1];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  S.l_part += lsum;
-  S.c_part += csum;
-  f16x8 av = load_v_op<PolBF16, D>(sm, vbuf, 0, st_cur, 0, lane);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int k = 0; k < 2 * ND; ++k) {
-    const int s2 = k / ND, dt = k % ND;
-    f16x8 an = av;
-    if (k + 1 < 2 * ND) an = load_v_op<PolBF16, D>(sm, vbuf, (k + 1) % ND, st_cur, (k + 1) / ND, lane);
-    S.oacc[dt] = PolBF16::mma_v(av, pop[s2], S.oacc[dt]);
-    S.uacc[dt] = PolBF16::mma_v(av, prop[s2], S.uacc[dt]);
-    av = an;
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
 template <class Pol, int D>
 __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     const typename Pol::in_t* __restrict__ q, const typename Pol::in_t* __restrict__ k,
@@ -466,48 +392,24 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
   S.m_run = -INFINITY;
   S.l_part = S.c_part = S.e_part = 0.f;
 
-  // Software pipeline over 32-key sub-tiles t: the score MFMAs of t+1 are
-  // issued before the softmax and value MFMAs of t.
-  // Two score register sets with fixed roles: set A holds the even sub-tile
-  // 2j, set B the odd sub-tile 2j+1 of 64-key iteration j.  With kPipe the
-  // scores of the next sub-tile are issued before the softmax of the current.
-  constexpr bool kPipe = v_rowmajor<Pol>();
-  f32x16 sa, ra, sb, rb;
-  if constexpr (kPipe) score_sub<Pol, D>(sm, 0, 0, col, half, qop, rop, sa, ra);
-  __syncthreads();  // K(0) fully read before iteration 0 may refill its buffer
-
+  f32x16 sa, ra;
   for (int j = 0; j < ntiles; ++j) {
     const int key0 = j * FWD_BC;
     const bool has_next_k = j + 2 < ntiles;
     const bool has_next_v = j + 1 < ntiles;
     if (has_next_k) gload_k<Pol, D>(pre, kp, key0 + 2 * FWD_BC, T);
     if (has_next_v) gload_v<Pol, D>(pre, vp, key0 + FWD_BC, T);
-    const int t0 = 2 * j;
-    if constexpr (kPipe) {
-      // sub-tile 2j (set A) while the scores of 2j+1 (set B) are computed
-      if (t0 < nsub) {
-        const float m_use = softmax_stats<Pol, D>(S, key0, qw, my_q, half, scale_log2, sa);
-        subtile_step_bf16<D>(S, sm, j & 1, 1, j & 1, 0, col, half, lane, scale_log2, m_use, qop, rop,
-                             sa, ra, sb, rb);
-      }
-      // sub-tile 2j+1 (set B) while the scores of 2j+2 (set A) are computed
-      if (t0 + 1 < nsub) {
-        const float m_use = softmax_stats<Pol, D>(S, key0 + 32, qw, my_q, half, scale_log2, sb);
-        subtile_step_bf16<D>(S, sm, (j + 1) & 1, 0, j & 1, 1, col, half, lane, scale_log2, m_use,
-                             qop, rop, sb, rb, sa, ra);
-      }
-    } else {
-      if (t0 < nsub) {
-        score_sub<Pol, D>(sm, j & 1, 0, col, half, qop, rop, sa, ra);
-        const float m_use = softmax_stats<Pol, D>(S, key0, qw, my_q, half, scale_log2, sa);
-        softmax_pv_body<Pol, D>(S, sm, j & 1, 0, lane, scale_log2, m_use, sa, ra);
-      }
-      if (t0 + 1 < nsub) {
-        score_sub<Pol, D>(sm, j & 1, 1, col, half, qop, rop, sb, rb);
-        const float m_use = softmax_stats<Pol, D>(S, key0 + 32, qw, my_q, half, scale_log2, sb);
-        softmax_pv_body<Pol, D>(S, sm, j & 1, 1, lane, scale_log2, m_use, sb, rb);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if (2 * j + st < nsub) {
+        score_sub<Pol, D>(sm, j & 1, st, col, half, qop, rop, sa, ra);
+        const float m_use = softmax_stats<Pol, D>(S, key0 + 32 * st, qw, my_q, half, scale_log2, sa);
+        softmax_pv_body<Pol, D>(S, sm, j & 1, st, lane, scale_log2, m_use, sa, ra);
       }
     }
+    // every wave has read K buffer j&1 (refilled with K(j+2)) and V buffer
+    // (j+1)&1 was last read in iteration j-1
+    __syncthreads();
     if (has_next_k) lds_put_k<Pol, D>(sm, j & 1, pre);
     if (has_next_v) lds_put_v<Pol, D>(sm, (j + 1) & 1, pre);
     __syncthreads();
@@ -544,6 +446,295 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 forward on 16x16x32 MFMA tiles, two waves per SIMD.
+//
+// A wave owns 16 query rows (one per lane column c = lane % 16; the four
+// 16-lane groups g = lane / 16 split the keys and the head dimension), so its
+// state is half that of a 32-row wave: O^T and U^T (D x 16, fp32) take D/2
+// registers each, the Q and rho B operands D/4 each.  The wave fits in 256
+// registers and two waves share every SIMD: while one runs its softmax on the
+// VALU the other feeds the matrix core (a wave raises its issue priority for
+// its MFMA runs so that the matrix core is served first).
+// Per 32-key sub-tile:
+//   S^T, R^T (32 keys x 16 queries) = K [Q; rho]^T: 2 key tiles x D/32 steps,
+//     A = K rows from LDS (ds_read_b128), B = Q / rho from registers;
+//     acc[t][j] is key 16 t + 4 g + j, query c;
+//   softmax in registers: 8 in-lane values per query, then the four 16-lane
+//     groups through permlane swaps (no LDS round trip);
+//   l and C as MFMAs against an all-ones A operand (every row of the result
+//     is the column sum over the keys of the rounded P / P.R);
+//   [O|U]^T += V^T [P | P.R]^T: D/16 d tiles, A = V^T from ds_read_b64_tr_b16,
+//     element e of group g is key 16 (e / 4) + 4 g + e % 4, matching P's order.
+// Workgroup: 8 waves, 128 query rows of one (b, h).  Tiles of 64 keys are
+// triple-buffered in LDS (K bf16 rows, V fp16 rows), with the global loads
+// issued two tiles ahead into alternating register sets: one barrier per tile.
+template <int D>
+struct Fwd16Smem {
+  // row strides (elements), chosen so that the ds_read_b128 of K and the
+  // transpose reads of V are free of bank conflicts (measured)
+  static constexpr int KLD = D + 16;
+  static constexpr int VLD = D + 16;
+  alignas(16) uint16_t k[3][FWD_BC * KLD];
+  alignas(16) _Float16 v[3][FWD_BC * VLD];
+};
+
+__device__ __forceinline__ f16x4 tr16_f16(const _Float16* p) {
+  s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(f16x4, t);
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ rho, float* __restrict__ o, float* __restrict__ lse,
+    float* __restrict__ c_aux, float* __restrict__ vbar_aux, int B, int Hq, int Hkv, int T,
+    float scale_log2) {
+  constexpr int NT = 64 * NW;       // threads
+  constexpr int BR = 16 * NW;       // query rows per workgroup
+  constexpr int NS = D / 32;        // score MFMA steps over d
+  constexpr int ND = D / 16;        // 16-row d tiles of O^T / U^T
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int NCH = FWD_BC * CPR / NT;  // chunks per thread per tile
+  using SM = Fwd16Smem<D>;
+  __shared__ SM sm;
+
+  const int nqb = (T + BR - 1) / BR;
+  const int bh_count = B * Hq;
+  const int lin = xcd_block_order(blockIdx.x, bh_count, nqb * bh_count);
+  const int qb = nqb - 1 - lin / bh_count;  // longest causal rows first
+  const int bh = lin % bh_count;
+  const int b = bh / Hq, h = bh % Hq;
+  const int hk = h / (Hq / Hkv);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int q0 = qb * BR;
+  const int qw = q0 + 16 * wave;  // first query of this wave
+  const int my_q = qw + c;
+
+  const uint16_t* qp = q + ((size_t)bh * T) * D;
+  const uint16_t* rp = rho + ((size_t)bh * T) * D;
+  const uint16_t* kp = k + ((size_t)(b * Hkv + hk) * T) * D;
+  const uint16_t* vp = v + ((size_t)(b * Hkv + hk) * T) * D;
+
+  const int kend = min(T, q0 + BR);
+  const int ntiles = (kend + FWD_BC - 1) / FWD_BC;
+  // 32-key sub-tiles this wave attends to: keys [0, min(kend, qw + 16))
+  const int nsub = (min(kend, qw + 16) + 31) / 32;
+
+  // global -> register prefetch of one K / V tile (rows past T read row T-1:
+  // finite, and masked by the causal test since they follow every query)
+  struct Pre { u32x4 k[NCH], v[NCH]; };
+  Pre preA, preB;
+  auto gload = [&](Pre& p, int key0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int it = threadIdx.x + NT * i;
+      const int row = it / CPR, cc = (it % CPR) * 8;
+      const size_t off = (size_t)min(key0 + row, T - 1) * D + cc;
+      p.k[i] = *reinterpret_cast<const u32x4*>(kp + off);
+      p.v[i] = *reinterpret_cast<const u32x4*>(vp + off);
+    }
+  };
+  auto lds_put = [&](const Pre& p, int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int it = threadIdx.x + NT * i;
+      const int row = it / CPR, cc = (it % CPR) * 8;
+      *reinterpret_cast<u32x4*>(&sm.k[buf][row * SM::KLD + cc]) = p.k[i];
+      const u16x8 bits = __builtin_bit_cast(u16x8, p.v[i]);
+      f16x8 hv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = bf16_bits_to_f16(bits[e]);
+      *reinterpret_cast<f16x8*>(&sm.v[buf][row * SM::VLD + cc]) = hv;
+    }
+  };
+
+  // prologue: tile 0 -> buffer 0; tile 1 in flight (register set B)
+  gload(preA, 0);
+  bf16x8 qop[NS], rop[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    u32x4 qa = {0u, 0u, 0u, 0u}, ra = {0u, 0u, 0u, 0u};
+    if (my_q < T) {
+      qa = *reinterpret_cast<const u32x4*>(qp + (size_t)my_q * D + 32 * s + 8 * g);
+      ra = *reinterpret_cast<const u32x4*>(rp + (size_t)my_q * D + 32 * s + 8 * g);
+    }
+    qop[s] = __builtin_bit_cast(bf16x8, qa);
+    rop[s] = __builtin_bit_cast(bf16x8, ra);
+  }
+  lds_put(preA, 0);
+  if (ntiles > 1) gload(preB, FWD_BC);
+  __syncthreads();
+
+  f32x4 oacc[ND], uacc[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    oacc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    uacc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+  // l and C as MFMAs against an all-ones A operand: every row of lacc / cacc
+  // holds the column (query) sum over the keys of the rounded P / P.R
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f}, cacc = {0.f, 0.f, 0.f, 0.f};
+  f16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.f;
+  // e_part: this lane's unrounded sum of p (the LSE only)
+  float m_run = -INFINITY, e_part = 0.f;
+
+  auto subtile = [&](int kbuf, int vbuf, int st, int kbase) {
+    // scores
+    __builtin_amdgcn_s_setprio(1);
+    f32x4 sacc[2], racc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t* krow = &sm.k[kbuf][(32 * st + 16 * t + c) * SM::KLD + 8 * g];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 32 * s));
+        const f32x4 zs = s == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : sacc[t];
+        const f32x4 zr = s == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : racc[t];
+        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[s], zs, 0, 0, 0);
+        racc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rop[s], zr, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // causal mask where the sub-tile reaches past the wave's first query
+    if (kbase + 31 > qw) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (kbase + 16 * t + 4 * g + j > my_q) sacc[t][j] = -INFINITY;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mt = fmaxf(mt, sacc[t][j]);
+    {
+      // max over the four 16-lane groups: permlane swaps, no LDS round trip
+      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+      mt = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+      mt = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    }
+    mt *= scale_log2;
+    // lazy rescale: the reference max moves only when a row's max exceeds it
+    // by more than kRescaleLog2, so p <= 2^kRescaleLog2 in between
+    if (__any(mt > m_run + kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float m_u = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_u);
+      e_part *= alpha;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        lacc[jj] *= alpha;
+        cacc[jj] *= alpha;
+      }
+#pragma unroll
+      for (int i = 0; i < ND; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          oacc[i][j] *= alpha;
+          uacc[i][j] *= alpha;
+        }
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    f16x8 pop, prop;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float s0 = sacc[e >> 2][e & 3], s1 = sacc[e >> 2][(e & 3) + 1];
+      const float p0 = fast_exp2(__builtin_fmaf(s0, scale_log2, -m_use));
+      const float p1 = fast_exp2(__builtin_fmaf(s1, scale_log2, -m_use));
+      e_part += p0 + p1;
+      const f16x2 ph = {(_Float16)p0, (_Float16)p1};
+      const f16x2 rh = {(_Float16)(p0 * racc[e >> 2][e & 3]), (_Float16)(p1 * racc[e >> 2][(e & 3) + 1])};
+      pop[e] = ph[0];
+      pop[e + 1] = ph[1];
+      prop[e] = rh[0];
+      prop[e + 1] = rh[1];
+    }
+    __builtin_amdgcn_s_setprio(1);
+    lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop, lacc, 0, 0, 0);
+    cacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, prop, cacc, 0, 0, 0);
+    // value MFMAs
+    const _Float16* vt = &sm.v[vbuf][(32 * st + 4 * g + (c >> 2)) * SM::VLD + 4 * (c & 3)];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      const f16x4 v0 = tr16_f16(vt + 16 * dt), v1 = tr16_f16(vt + 16 * dt + 16 * SM::VLD);
+      f16x8 av;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        av[e] = v0[e];
+        av[4 + e] = v1[e];
+      }
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pop, oacc[dt], 0, 0, 0);
+      uacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, prop, uacc[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Tile j lives in buffer j % 3.  Iteration j issues the global loads of
+  // tile j+2 (register set j % 2) and stores tile j+1 (set (j+1) % 2, issued
+  // an iteration earlier) into buffer (j+1) % 3, last read in iteration j-2.
+  auto iter = [&](int j, Pre& issue, Pre& store) {
+    const int key0 = j * FWD_BC;
+    if (j + 2 < ntiles) gload(issue, key0 + 2 * FWD_BC);
+    const int buf = j % 3;
+    if (2 * j < nsub) subtile(buf, buf, 0, key0);
+    if (2 * j + 1 < nsub) subtile(buf, buf, 1, key0 + 32);
+    if (j + 1 < ntiles) lds_put(store, (j + 1) % 3);
+    __syncthreads();
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    iter(j, preA, preB);
+    if (j + 1 < ntiles) iter(j + 1, preB, preA);
+  }
+
+  // epilogue: o = (O/l)(1 + C/l) - U/l; LSE = ln sum exp(scaled scores)
+  const float l_tot = lacc[0], c_tot = cacc[0];
+  float e_tot = e_part;
+  e_tot += __shfl_xor(e_tot, 16, 64);
+  e_tot += __shfl_xor(e_tot, 32, 64);
+  const float inv = 1.f / l_tot;
+  const float cc = c_tot * inv;
+  if (my_q < T) {
+    float* orow = o + ((size_t)bh * T + my_q) * D;
+    float* vrow = vbar_aux ? vbar_aux + ((size_t)bh * T + my_q) * D : nullptr;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      f32x4 ov, vv;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float vbar = oacc[dt][jj] * inv;
+        vv[jj] = vbar;
+        ov[jj] = vbar * (1.f + cc) - uacc[dt][jj] * inv;
+      }
+      *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * g) = ov;
+      if (vrow) *reinterpret_cast<f32x4*>(vrow + 16 * dt + 4 * g) = vv;
+    }
+    if (g == 0) {
+      if (lse) lse[(size_t)bh * T + my_q] = (m_run + __log2f(e_tot)) * kLn2;
+      if (c_aux) c_aux[(size_t)bh * T + my_q] = cc;
+    }
+  }
+}
+
+template <int D, int NW>
+hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void* rho, float* o,
+                        float* lse, float* c_aux, float* vbar_aux, int B, int Hq, int Hkv, int T,
+                        float scale, hipStream_t stream) {
+  const int nqb = (T + 16 * NW - 1) / (16 * NW);
+  hipLaunchKernelGGL((fwd16_kernel<D, NW>), dim3(nqb * B * Hq), dim3(64 * NW), 0, stream,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)rho, o,
+                     lse, c_aux, vbar_aux, B, Hq, Hkv, T, scale * kLog2e);
+  return hipGetLastError();
+}
+
 template <class Pol, int D>
 hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const void* rho, float* o,
                         float* lse, float* c_aux, float* vbar_aux, int B, int Hq, int Hkv, int T,
@@ -563,8 +754,8 @@ hipError_t launch_fwd(int dtype, const void* q, const void* k, const void* v, co
                       float* o, float* lse, float* c_aux, float* vbar_aux, int B, int Hq, int Hkv,
                       int T, int d, float scale, hipStream_t stream) {
   if (dtype == PLX_BF16) {
-    if (d == 64) return launch_fwd_t<PolBF16, 64>(q, k, v, rho, o, lse, c_aux, vbar_aux, B, Hq, Hkv, T, scale, stream);
-    return launch_fwd_t<PolBF16, 128>(q, k, v, rho, o, lse, c_aux, vbar_aux, B, Hq, Hkv, T, scale, stream);
+    if (d == 64) return launch_fwd16<64, FWD16_WAVES>(q, k, v, rho, o, lse, c_aux, vbar_aux, B, Hq, Hkv, T, scale, stream);
+    return launch_fwd16<128, FWD16_WAVES>(q, k, v, rho, o, lse, c_aux, vbar_aux, B, Hq, Hkv, T, scale, stream);
   }
   if (d == 64) return launch_fwd_t<PolF32, 64>(q, k, v, rho, o, lse, c_aux, vbar_aux, B, Hq, Hkv, T, scale, stream);
   return launch_fwd_t<PolF32, 128>(q, k, v, rho, o, lse, c_aux, vbar_aux, B, Hq, Hkv, T, scale, stream);
