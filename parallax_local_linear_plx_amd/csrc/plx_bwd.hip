@@ -391,6 +391,401 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 path.  Q, rho, dO, K and V enter both kernels' MFMAs as fp16: the
+// bf16 -> fp16 conversion is exact over fp16's normal range, and fp16
+// operands let one row-major LDS tile serve both the score GEMMs (rows read
+// with ds_read_b128) and the transposed value GEMMs (ds_read_b64_tr_b16).
+// Tiles are double-buffered: the next tile's global loads are issued at the
+// top of an iteration, converted and stored at its end (into the buffer read
+// one iteration earlier), followed by the iteration's single barrier.
+// Rows past T are loaded as row T-1 (finite) and given p = 0.
+constexpr int B16_LD = 24;  // row padding (halves): ds_read_b128 rows and transpose reads spread over the banks
+
+__device__ __forceinline__ f16x4 tr_read(const _Float16* p) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(f16x4, t);
+}
+
+// Value-GEMM A operand from a row-major fp16 tile: element e of lane
+// (column col0 + lane % 32, half h) is tile[row0 + acc_row(8 s + e, h)][col0 + lane % 32],
+// matching a B operand taken from slots 8 s .. 8 s + 7 of a 32x32 accumulator.
+// ds_read_b64_tr_b16 hands lane i of each 16-lane block element i % 4 of the
+// chunks addressed by lanes 4 e + i / 4 of that block.
+__device__ __forceinline__ f16x8 tr_op(const _Float16* tile, int ld, int row0, int col0, int s, int lane) {
+  const int h = lane >> 5, blk = (lane >> 4) & 1, li = lane & 15;
+  const _Float16* base = tile + (row0 + 16 * s + 4 * h + (li >> 2)) * ld + col0 + 16 * blk + 4 * (li & 3);
+  const f16x4 lo = tr_read(base), hi = tr_read(base + 8 * ld);
+  f16x8 a;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = lo[e];
+    a[4 + e] = hi[e];
+  }
+  return a;
+}
+
+__device__ __forceinline__ f16x8 cvt_bf16x8_f16(u32x4 raw) {
+  const u16x8 b = __builtin_bit_cast(u16x8, raw);
+  f16x8 h;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = bf16_bits_to_f16(b[e]);
+  return h;
+}
+
+__device__ __forceinline__ f32x16 mma16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// dQ and drho, query-outer (bf16).
+template <int D>
+__global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ rho, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
+    const float* __restrict__ c_aux, const float* __restrict__ Gv, const float* __restrict__ dlt,
+    float* __restrict__ dq, float* __restrict__ drho, int B, int Hq, int Hkv, int T, float scale,
+    float scale_log2) {
+  constexpr int NS = D / 16, ND = D / 32;
+  constexpr int LD = D + B16_LD;
+  constexpr int CPR = D / 8;
+  constexpr int NCH = DQ_BC * CPR / BWD_THREADS;  // 16-byte chunks per thread per tile and tensor
+  __shared__ alignas(16) _Float16 ks[2][DQ_BC * LD];
+  __shared__ alignas(16) _Float16 vs[2][DQ_BC * LD];
+
+  const int nqb = (T + DQ_BR - 1) / DQ_BR;
+  const int bh_count = B * Hq;
+  const int lin = xcd_block_order(blockIdx.x, bh_count, nqb * bh_count);
+  const int qb = nqb - 1 - lin / bh_count;
+  const int bh = lin % bh_count;
+  const int b = bh / Hq, h = bh % Hq;
+  const int hk = h / (Hq / Hkv);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int q0 = qb * DQ_BR;
+  const int qw = q0 + 32 * wave;
+  const int my_q = qw + col;
+  const bool qvalid = my_q < T;
+
+  const size_t rowbase = (size_t)bh * T;
+  const uint16_t* kp = k + ((size_t)(b * Hkv + hk) * T) * D;
+  const uint16_t* vp = v + ((size_t)(b * Hkv + hk) * T) * D;
+  const int kend = min(T, q0 + DQ_BR);
+  const int ntiles = (kend + DQ_BC - 1) / DQ_BC;
+
+  u32x4 pk[NCH], pv[NCH];
+  auto gload = [&](int key0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int it = threadIdx.x + BWD_THREADS * i;
+      const size_t off = (size_t)min(key0 + it / CPR, T - 1) * D + (it % CPR) * 8;
+      pk[i] = *reinterpret_cast<const u32x4*>(kp + off);
+      pv[i] = *reinterpret_cast<const u32x4*>(vp + off);
+    }
+  };
+  auto lds_put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int it = threadIdx.x + BWD_THREADS * i;
+      const int o = (it / CPR) * LD + (it % CPR) * 8;
+      *reinterpret_cast<f16x8*>(&ks[buf][o]) = cvt_bf16x8_f16(pk[i]);
+      *reinterpret_cast<f16x8*>(&vs[buf][o]) = cvt_bf16x8_f16(pv[i]);
+    }
+  };
+
+  gload(0);
+  f16x8 qop[NS], rop[NS], gop[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    u32x4 qa = {0u, 0u, 0u, 0u}, ra = qa, ga = qa;
+    if (qvalid) {
+      const size_t off = (rowbase + my_q) * D + 16 * s + 8 * half;
+      qa = *reinterpret_cast<const u32x4*>(q + off);
+      ra = *reinterpret_cast<const u32x4*>(rho + off);
+      ga = *reinterpret_cast<const u32x4*>(d_o + off);
+    }
+    qop[s] = cvt_bf16x8_f16(qa);
+    rop[s] = cvt_bf16x8_f16(ra);
+    gop[s] = cvt_bf16x8_f16(ga);
+  }
+  const float lse2 = qvalid ? lse[rowbase + my_q] * kLog2e : 0.f;
+  const float ci = qvalid ? c_aux[rowbase + my_q] : 0.f;
+  const float Gi = qvalid ? Gv[rowbase + my_q] : 0.f;
+  const float di = qvalid ? dlt[rowbase + my_q] : 0.f;
+  lds_put(0);
+  __syncthreads();
+
+  f32x16 dqa[ND], dra[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    dqa[i] = zero16();
+    dra[i] = zero16();
+  }
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int key0 = j * DQ_BC;
+    const int buf = j & 1;
+    if (j + 1 < ntiles) gload(key0 + DQ_BC);
+    if (key0 <= qw + 31) {
+      f32x16 sa[2], ra[2], aa[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        sa[st] = ra[st] = aa[st] = zero16();
+        const _Float16* krow = &ks[buf][(32 * st + col) * LD + 8 * half];
+        const _Float16* vrow = &vs[buf][(32 * st + col) * LD + 8 * half];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const f16x8 ak = *reinterpret_cast<const f16x8*>(krow + 16 * s);
+          const f16x8 av = *reinterpret_cast<const f16x8*>(vrow + 16 * s);
+          sa[st] = mma16(ak, qop[s], sa[st]);
+          ra[st] = mma16(ak, rop[s], ra[st]);
+          aa[st] = mma16(av, gop[s], aa[st]);
+        }
+      }
+      // dS^T and dR^T in place of S^T and R^T
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const int key = key0 + 32 * st + acc_row(a, half);
+          float p = fast_exp2(__builtin_fmaf(sa[st][a], scale_log2, -lse2));
+          if (key > my_q || !qvalid) p = 0.f;
+          const float r = ra[st][a], A = aa[st][a];
+          const float f = 1.f + ci - r;
+          sa[st][a] = p * (f * A - Gi + di * (r - ci));
+          ra[st][a] = -p * (A - di);
+        }
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          f16x8 dsop, drop;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            dsop[e] = (_Float16)sa[st][8 * s + e];
+            drop[e] = (_Float16)ra[st][8 * s + e];
+          }
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt) {
+            const f16x8 a = tr_op(ks[buf], LD, 32 * st, 32 * dt, s, lane);
+            dqa[dt] = mma16(a, dsop, dqa[dt]);
+            dra[dt] = mma16(a, drop, dra[dt]);
+          }
+        }
+    }
+    if (j + 1 < ntiles) lds_put((j + 1) & 1);  // buffer last read in iteration j-1
+    __syncthreads();
+  }
+
+  if (qvalid) {
+    float* dqr = dq + (rowbase + my_q) * D;
+    float* drr = drho + (rowbase + my_q) * D;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * dt + 8 * i + 4 * half;
+        f32x4 x, y;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          x[jj] = scale * dqa[dt][4 * i + jj];
+          y[jj] = dra[dt][4 * i + jj];
+        }
+        *reinterpret_cast<f32x4*>(dqr + d0) = x;
+        *reinterpret_cast<f32x4*>(drr + d0) = y;
+      }
+  }
+}
+
+// dK and dV, key-outer (bf16): the query tiles of all G heads of the KV head
+// form one sequence, prefetched one tile ahead.
+template <int D>
+__global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ rho, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
+    const float* __restrict__ c_aux, const float* __restrict__ Gv, const float* __restrict__ dlt,
+    float* __restrict__ dk, float* __restrict__ dv, int B, int Hq, int Hkv, int T, float scale,
+    float scale_log2) {
+  constexpr int BQ = 64;
+  constexpr int NS = D / 16, ND = D / 32;
+  constexpr int LD = D + B16_LD;
+  constexpr int CPR = D / 8;
+  constexpr int NCH = BQ * CPR / BWD_THREADS;
+  __shared__ alignas(16) _Float16 qs_[2][BQ * LD];
+  __shared__ alignas(16) _Float16 rs_[2][BQ * LD];
+  __shared__ alignas(16) _Float16 gs_[2][BQ * LD];
+  __shared__ alignas(16) float sc_[2][4][BQ];  // lse * log2e, c, G, delta
+
+  const int bhk_count = B * Hkv;
+  const int lin = blockIdx.x;
+  const int kb = lin / bhk_count;
+  const int bhk = lin % bhk_count;
+  const int b = bhk / Hkv, hk = bhk % Hkv;
+  const int G = Hq / Hkv;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const int k0 = kb * KV_BK;
+  const int kw = k0 + 32 * wave;
+  const int my_k = kw + col;
+  const bool kvalid = my_k < T;
+
+  const size_t kvbase = (size_t)bhk * T;
+  const int nqt = (T - k0 + BQ - 1) / BQ;  // query tiles per head (queries >= k0)
+  const int ntile = G * nqt;
+
+  u32x4 pq[NCH], pr[NCH], pg[NCH];
+  float psc[4];
+  auto tile_rows = [&](int n, size_t& rowbase, int& qt0) {
+    const int hh = n / nqt;
+    qt0 = k0 + (n - hh * nqt) * BQ;
+    rowbase = ((size_t)b * Hq + hk * G + hh) * T;
+  };
+  auto gload = [&](int n) {
+    size_t rowbase;
+    int qt0;
+    tile_rows(n, rowbase, qt0);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int it = threadIdx.x + BWD_THREADS * i;
+      const size_t off = (rowbase + min(qt0 + it / CPR, T - 1)) * D + (it % CPR) * 8;
+      pq[i] = *reinterpret_cast<const u32x4*>(q + off);
+      pr[i] = *reinterpret_cast<const u32x4*>(rho + off);
+      pg[i] = *reinterpret_cast<const u32x4*>(d_o + off);
+    }
+    if (threadIdx.x < BQ) {
+      const size_t r = rowbase + min(qt0 + (int)threadIdx.x, T - 1);
+      psc[0] = lse[r] * kLog2e;
+      psc[1] = c_aux[r];
+      psc[2] = Gv[r];
+      psc[3] = dlt[r];
+    }
+  };
+  auto lds_put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int it = threadIdx.x + BWD_THREADS * i;
+      const int o = (it / CPR) * LD + (it % CPR) * 8;
+      *reinterpret_cast<f16x8*>(&qs_[buf][o]) = cvt_bf16x8_f16(pq[i]);
+      *reinterpret_cast<f16x8*>(&rs_[buf][o]) = cvt_bf16x8_f16(pr[i]);
+      *reinterpret_cast<f16x8*>(&gs_[buf][o]) = cvt_bf16x8_f16(pg[i]);
+    }
+    if (threadIdx.x < BQ) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) sc_[buf][m][threadIdx.x] = psc[m];
+    }
+  };
+
+  gload(0);
+  f16x8 kop[NS], vop[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    u32x4 ka = {0u, 0u, 0u, 0u}, va = ka;
+    if (kvalid) {
+      const size_t off = (kvbase + my_k) * D + 16 * s + 8 * half;
+      ka = *reinterpret_cast<const u32x4*>(k + off);
+      va = *reinterpret_cast<const u32x4*>(v + off);
+    }
+    kop[s] = cvt_bf16x8_f16(ka);
+    vop[s] = cvt_bf16x8_f16(va);
+  }
+  lds_put(0);
+  __syncthreads();
+
+  f32x16 dka[ND], dva[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    dka[i] = zero16();
+    dva[i] = zero16();
+  }
+
+  for (int n = 0; n < ntile; ++n) {
+    const int buf = n & 1;
+    size_t rowbase_unused;
+    int qt0;
+    tile_rows(n, rowbase_unused, qt0);
+    if (n + 1 < ntile) gload(n + 1);
+#pragma unroll
+    for (int st = 0; st < BQ / 32; ++st) {
+      const int qs = qt0 + 32 * st;
+      if (qs + 31 < kw) continue;  // every query of the sub-tile precedes every key of the wave
+      f32x16 sa = zero16(), ra = zero16(), aa = zero16();
+      const _Float16* qrow = &qs_[buf][(32 * st + col) * LD + 8 * half];
+      const _Float16* rrow = &rs_[buf][(32 * st + col) * LD + 8 * half];
+      const _Float16* grow = &gs_[buf][(32 * st + col) * LD + 8 * half];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        sa = mma16(*reinterpret_cast<const f16x8*>(qrow + 16 * s), kop[s], sa);
+        ra = mma16(*reinterpret_cast<const f16x8*>(rrow + 16 * s), kop[s], ra);
+        aa = mma16(*reinterpret_cast<const f16x8*>(grow + 16 * s), vop[s], aa);
+      }
+      // lane column = key my_k; accumulator slot a = query qs + acc_row(a, half)
+      float pt[16], ds[16], dr[16];
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int r0 = 32 * st + 8 * i4 + 4 * half;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sc_[buf][0][r0]);
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(&sc_[buf][1][r0]);
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(&sc_[buf][2][r0]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sc_[buf][3][r0]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int a = 4 * i4 + jj;
+          const int qi = qt0 + r0 + jj;
+          float p = fast_exp2(__builtin_fmaf(sa[a], scale_log2, -l4[jj]));
+          if (qi < my_k || qi >= T) p = 0.f;
+          const float r = ra[a], A = aa[a];
+          const float f = 1.f + c4[jj] - r;
+          pt[a] = p * f;
+          ds[a] = scale * p * (f * A - g4[jj] + d4[jj] * (r - c4[jj]));
+          dr[a] = -p * (A - d4[jj]);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        f16x8 pop, dsop, drop;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pop[e] = (_Float16)pt[8 * s + e];
+          dsop[e] = (_Float16)ds[8 * s + e];
+          drop[e] = (_Float16)dr[8 * s + e];
+        }
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+          const f16x8 ag = tr_op(gs_[buf], LD, 32 * st, 32 * dt, s, lane);
+          const f16x8 aq = tr_op(qs_[buf], LD, 32 * st, 32 * dt, s, lane);
+          const f16x8 ar = tr_op(rs_[buf], LD, 32 * st, 32 * dt, s, lane);
+          dva[dt] = mma16(ag, pop, dva[dt]);
+          dka[dt] = mma16(aq, dsop, dka[dt]);
+          dka[dt] = mma16(ar, drop, dka[dt]);
+        }
+      }
+    }
+    if (n + 1 < ntile) lds_put((n + 1) & 1);  // buffer last read in iteration n-1
+    __syncthreads();
+  }
+
+  if (kvalid) {
+    float* dkr = dk + (kvbase + my_k) * D;
+    float* dvr = dv + (kvbase + my_k) * D;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * dt + 8 * i + 4 * half;
+        f32x4 x, y;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          x[jj] = dka[dt][4 * i + jj];
+          y[jj] = dva[dt][4 * i + jj];
+        }
+        *reinterpret_cast<f32x4*>(dkr + d0) = x;
+        *reinterpret_cast<f32x4*>(dvr + d0) = y;
+      }
+  }
+}
+
 template <class Pol, int D>
 hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* rho,
                         const void* d_o, const float* o, const float* lse, const float* c_aux,
@@ -405,18 +800,32 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nqb = (T + DQ_BR - 1) / DQ_BR;
-  hipLaunchKernelGGL((bwd_dq_kernel<Pol, D>), dim3(nqb * B * Hq), dim3(BWD_THREADS), 0, stream,
-                     (const in_t*)q, (const in_t*)k, (const in_t*)v, (const in_t*)rho,
-                     (const in_t*)d_o, lse, c_aux, G, dl, dq, drho, B, Hq, Hkv, T, scale,
-                     scale * kLog2e);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int nkb = (T + KV_BK - 1) / KV_BK;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<Pol, D>), dim3(nkb * B * Hkv), dim3(BWD_THREADS), 0, stream,
-                     (const in_t*)q, (const in_t*)k, (const in_t*)v, (const in_t*)rho,
-                     (const in_t*)d_o, lse, c_aux, G, dl, dk, dv, B, Hq, Hkv, T, scale,
-                     scale * kLog2e);
-  return hipGetLastError();
+  if constexpr (sizeof(in_t) == 2) {
+    hipLaunchKernelGGL((bwd_dq16_kernel<D>), dim3(nqb * B * Hq), dim3(BWD_THREADS), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)rho,
+                       (const uint16_t*)d_o, lse, c_aux, G, dl, dq, drho, B, Hq, Hkv, T, scale,
+                       scale * kLog2e);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv16_kernel<D>), dim3(nkb * B * Hkv), dim3(BWD_THREADS), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)rho,
+                       (const uint16_t*)d_o, lse, c_aux, G, dl, dk, dv, B, Hq, Hkv, T, scale,
+                       scale * kLog2e);
+    return hipGetLastError();
+  } else {
+    hipLaunchKernelGGL((bwd_dq_kernel<Pol, D>), dim3(nqb * B * Hq), dim3(BWD_THREADS), 0, stream,
+                       (const in_t*)q, (const in_t*)k, (const in_t*)v, (const in_t*)rho,
+                       (const in_t*)d_o, lse, c_aux, G, dl, dq, drho, B, Hq, Hkv, T, scale,
+                       scale * kLog2e);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<Pol, D>), dim3(nkb * B * Hkv), dim3(BWD_THREADS), 0, stream,
+                       (const in_t*)q, (const in_t*)k, (const in_t*)v, (const in_t*)rho,
+                       (const in_t*)d_o, lse, c_aux, G, dl, dk, dv, B, Hq, Hkv, T, scale,
+                       scale * kLog2e);
+    return hipGetLastError();
+  }
 }
 
 }  // namespace
