@@ -15,7 +15,7 @@ synchronisations.  The CPU baseline is the fp64 oracle on a bounded sample of
 prefill rows, timed on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--only all|prefill|decode|decode_long|train|copy] [--no-cpu]
+                       [--only all|prefill|decode|decode_long|train|copy] [--no-cpu] [--no-graph]
 """
 
 from __future__ import annotations
@@ -58,6 +58,26 @@ def time_steps(fn, steps, warmup):
     return start.elapsed_time(stop) / steps
 
 
+def time_graph_steps(fn, per_graph, replays, warmup):
+    """Average ms per call of fn when `per_graph` calls are captured in one HIP
+    graph and the graph is replayed `replays` times (launch gaps removed)."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            fn()
+    ms = time_steps(graph.replay, replays, warmup)
+    del graph
+    return ms / per_graph
+
+
 def causal_pairs(T):
     return T * (T + 1) // 2
 
@@ -90,7 +110,7 @@ def bench_prefill(steps, warmup):
 
 
 # ------------------------------------------------------------------- decode
-def bench_decode(steps, warmup, B, ctx_len, S_max, name, seed):
+def bench_decode(steps, warmup, B, ctx_len, S_max, name, seed, graph=True):
     import torch
 
     from parallax_local_linear_plx_amd import inputs, plx_decode
@@ -110,6 +130,8 @@ def bench_decode(steps, warmup, B, ctx_len, S_max, name, seed):
         plx_decode(q, rho, kc, vc, ctx, num_splits=0, workspace=ws, o=o, lse=False)
 
     ms = time_steps(step, steps, warmup)
+    # the same steps captured ten to a graph, as a serving loop would replay them
+    ms_graph = time_graph_steps(step, 10, max(1, steps // 10), max(1, warmup // 10)) if graph else None
     kv_bytes = int(np.sum(ctx_len)) * Hkv * d * 2 * 2
     io_bytes = B * Hq * d * (2 + 2 + 4)
     gbs = (kv_bytes + io_bytes) / (ms * 1e-3) / 1e9
@@ -118,6 +140,8 @@ def bench_decode(steps, warmup, B, ctx_len, S_max, name, seed):
     torch.cuda.empty_cache()
     return {"workload": name, "us_per_step": ms * 1e3, "us_per_token": ms * 1e3,
             "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS, "bytes": kv_bytes + io_bytes,
+            "us_per_step_graph10": ms_graph * 1e3 if graph else None,
+            "GB/s_graph10": (kv_bytes + io_bytes) / (ms_graph * 1e-3) / 1e9 if graph else None,
             "flop_per_byte": flops / (kv_bytes + io_bytes),
             "ctx_len_sum": int(np.sum(ctx_len))}
 
@@ -259,6 +283,7 @@ def main():
     ap.add_argument("--only", default="all",
                     choices=["all", "prefill", "decode", "decode_long", "train", "copy"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay decode timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -286,7 +311,7 @@ def main():
     if args.only in ("all", "decode"):
         log("decode B64 ctx8192 ...")
         res["decode"] = bench_decode(args.steps, args.warmup, 64, [8192] * 64, 8192,
-                                     "bf16 decode B=64 Hq=16 Hkv=8 ctx=8192 d=128", 31)
+                                     "bf16 decode B=64 Hq=16 Hkv=8 ctx=8192 d=128", 31, not args.no_graph)
         log(f"  {res['decode']['us_per_step']:.1f} us  {res['decode']['GB/s']:.0f} GB/s")
     if args.only in ("all", "decode_long"):
         from parallax_local_linear_plx_amd import inputs
@@ -295,7 +320,7 @@ def main():
         log(f"long decode B8 ctx {ctx.tolist()} ...")
         res["decode_long"] = bench_decode(args.steps, args.warmup, 8, ctx, 131072,
                                           "bf16 long-context decode B=8 Hq=16 Hkv=8 "
-                                          "ctx~U{16384..131072} d=128, split-K", 41)
+                                          "ctx~U{16384..131072} d=128, split-K", 41, not args.no_graph)
         log(f"  {res['decode_long']['us_per_step']:.1f} us  {res['decode_long']['GB/s']:.0f} GB/s")
     if args.only in ("all", "train"):
         log("training step ...")

@@ -66,13 +66,14 @@ size_t plx_decode_workspace_size(int B, int Hq, int Hkv, int S_max, int d, int n
   if (ns > S_max) ns = S_max;
   const int chunk = plx::decode_chunk_keys(S_max, ns);
   ns = (S_max + chunk - 1) / chunk;
-  size_t recs = (size_t)B * Hq * ns;
+  size_t bytes = (size_t)B * Hq * ns * plx::decode_record_floats(d) * sizeof(float);
   if (num_splits == 0) {
     // automatic: bf16 runs the balanced schedule, fp32 the automatic split count
-    const size_t bal = plx::decode_balanced_records(B, Hq, Hkv, S_max);
-    if (bal > recs) recs = bal;
+    const size_t bal =
+        plx::decode_balanced_records(B, Hq, Hkv, S_max) * plx::decode_record_floats(d) * sizeof(float);
+    if (bal > bytes) bytes = bal;
   }
-  return recs * plx::decode_record_floats(d) * sizeof(float);
+  return bytes;
 }
 
 plx_status plx_decode(const void* q, const void* rho, const void* k_cache, const void* v_cache,

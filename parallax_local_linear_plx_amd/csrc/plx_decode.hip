@@ -320,6 +320,13 @@ __device__ __forceinline__ long long wave_sum_ll(long long x) {
 // Start of the balanced range of workgroup w of P, in keys of the flattened space.
 __device__ __forceinline__ long long bal_lo(long long w, long long W, int P) { return w * W / P; }
 
+// Workgroup whose range holds key x of the flattened space: the largest w with
+// bal_lo(w) <= x, i.e. w W < (x + 1) P.
+__device__ __forceinline__ long long bal_wg(long long x, long long W, int P) {
+  const long long w = ((x + 1) * P - 1) / W;
+  return w < P - 1 ? w : P - 1;
+}
+
 // Total keys of the flattened space: Hkv * sum of valid lengths (every lane).
 __device__ long long bal_total(const int32_t* __restrict__ ctx_len, int B, int Hkv, int S_max) {
   const int lane = threadIdx.x & 63;
@@ -552,6 +559,75 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_chunk_kernel(
                     (size_t)nsplit * REC);
 }
 
+// One wave merges the n records of one head (record i at rec0 + i * stride;
+// a record with valid(i) false was never written and is skipped) into
+//   o = (O/l)(1 + C/l) - U/l,   LSE = M + ln e   (natural log).
+// Lane j holds elements j * D/64 ..; every record's O and U loads are issued
+// unconditionally (the slots lie inside the workspace) so that they overlap.
+template <int D, class Valid>
+__device__ __forceinline__ void wave_merge(const float* __restrict__ rec0, size_t stride, int n,
+                                           Valid valid, float* __restrict__ orow,
+                                           float* __restrict__ lse_out) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  float M = -INFINITY;
+  for (int i = lane; i < n; i += 64)
+    if (valid(i)) M = fmaxf(M, rec0[(size_t)i * stride]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  float l = 0.f, e = 0.f, C = 0.f, O[EPL], U[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) O[j] = U[j] = 0.f;
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    float a = 0.f;
+    if (i < n && valid(i)) {
+      const float* r = rec0 + (size_t)i * stride;
+      a = fast_exp2(r[0] - M);
+      l += a * r[1];
+      e += a * r[2];
+      C += a * r[3];
+    }
+    const int cnt = min(64, n - base);
+    for (int k0 = 0; k0 < cnt; k0 += 8) {
+      // eight records per step, loads first; past the end the last record is
+      // read again with weight zero
+      float ak[8], ov[8][EPL], uv[8][EPL];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = k0 + j;
+        ak[j] = k < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), k & 63)) : 0.f;
+        const float* r = rec0 + (size_t)min(base + k, n - 1) * stride + 4 + lane * EPL;
+        if constexpr (EPL == 2) {
+          const float2 o2 = *reinterpret_cast<const float2*>(r);
+          const float2 u2 = *reinterpret_cast<const float2*>(r + D);
+          ov[j][0] = o2.x, ov[j][1] = o2.y, uv[j][0] = u2.x, uv[j][1] = u2.y;
+        } else {
+          ov[j][0] = r[0], uv[j][0] = r[D];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          // a record that was never written (weight 0) may hold anything
+          O[i] = ak[j] != 0.f ? __builtin_fmaf(ak[j], ov[j][i], O[i]) : O[i];
+          U[i] = ak[j] != 0.f ? __builtin_fmaf(ak[j], uv[j][i], U[i]) : U[i];
+        }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    l += __shfl_xor(l, off, 64);
+    e += __shfl_xor(e, off, 64);
+    C += __shfl_xor(C, off, 64);
+  }
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) orow[lane * EPL + j] = O[j] * inv * (1.f + C * inv) - U[j] * inv;
+  if (lse_out && lane == 0) *lse_out = (M + __log2f(e)) * kLn2;
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_balanced_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ rho, const uint16_t* __restrict__ kc,
@@ -599,8 +675,8 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_balanced_kernel(
   while (true) {
     const int k_end = (int)min((long long)len, key + (hi - pos));
     const int hq0 = hk * Gfull + hoff;
-    const long long slot = (long long)blockIdx.x + (long long)b * Hkv + hk;
-    float* rec = part + ((size_t)slot * Gfull + hoff) * REC;
+    const long long seg = (long long)b * Hkv + hk;
+    float* rec = part + ((size_t)(blockIdx.x + seg) * Gfull + hoff) * REC;
     dec16_range<D, G>(sm, q, rho, kc, vc, b, hk, hq0, Hq, Hkv, S_max, key, k_end, scale_log2, rec, REC);
     pos += k_end - key;
     if (pos >= hi) break;
@@ -632,149 +708,67 @@ hipError_t launch_partial16(const void* q, const void* rho, const void* kc, cons
   return hipGetLastError();
 }
 
-// Merge: rescale a head's n records to their common max M and finish
-//   o = (O/l)(1 + C/l) - U/l,   LSE = M + ln e   (natural log).
-// Record i sits at rec0 + i * stride; a record with valid(i) false was never
-// written and is skipped.  The block (one thread per output element) reads the
-// record headers in parallel and then streams O and U with independent loads.
-template <int D, class Valid>
-__device__ __forceinline__ void merge_records(const float* __restrict__ rec0, size_t stride, int n,
-                                              Valid valid, float* __restrict__ orow,
-                                              float* __restrict__ lse_out) {
-  constexpr int NW = D / 64;
-  __shared__ float red[4][NW];
-  __shared__ float scale_s[D];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  auto block_reduce = [&](float x, int slot, bool is_max) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float y = __shfl_xor(x, off, 64);
-      x = is_max ? fmaxf(x, y) : x + y;
-    }
-    if (lane == 0) red[slot][wave] = x;
-    __syncthreads();
-    float r = red[slot][0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) r = is_max ? fmaxf(r, red[slot][w]) : r + red[slot][w];
-    return r;
-  };
-  float M = -INFINITY;
-  for (int i = t; i < n; i += D)
-    if (valid(i)) M = fmaxf(M, rec0[(size_t)i * stride]);
-  M = block_reduce(M, 0, true);
-  float l = 0.f, e = 0.f, C = 0.f, O = 0.f, U = 0.f;
-  for (int base = 0; base < n; base += D) {
-    const int i = base + t;
-    float a = 0.f;
-    if (i < n && valid(i)) {
-      const float* r = rec0 + (size_t)i * stride;
-      a = fast_exp2(r[0] - M);
-      l += a * r[1];
-      e += a * r[2];
-      C += a * r[3];
-    }
-    __syncthreads();  // previous batch's scale_s reads are done
-    scale_s[t] = a;
-    __syncthreads();
-    const int cnt = min(D, n - base);
-#pragma unroll 4
-    for (int k = 0; k < cnt; ++k) {
-      const float ak = scale_s[k];
-      if (ak != 0.f) {
-        const float* r = rec0 + (size_t)(base + k) * stride;
-        O += ak * r[4 + t];
-        U += ak * r[4 + D + t];
-      }
-    }
-  }
-  l = block_reduce(l, 1, false);
-  e = block_reduce(e, 2, false);
-  C = block_reduce(C, 3, false);
-  const float inv = 1.f / l;
-  orow[t] = O * inv * (1.f + C * inv) - U * inv;
-  if (lse_out && t == 0) *lse_out = (M + __log2f(e)) * kLn2;
-}
-
-__device__ __forceinline__ void write_nan_row(float* orow, float* lse_out, int t) {
-  orow[t] = __builtin_nanf("");
-  if (lse_out && t == 0) *lse_out = __builtin_nanf("");
-}
-
 // Chunked schedule: the records of (b, h) are splits 0 .. ceil(ctx/chunk)-1.
+// A wave per head, four heads per block.
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_chunk_kernel(const float* __restrict__ part,
-                                                               const int32_t* __restrict__ ctx_len,
-                                                               float* __restrict__ o, float* __restrict__ lse,
-                                                               int Hq, int S_max, int chunk, int nsplit) {
+__global__ __launch_bounds__(256) void decode_merge_chunk_kernel(const float* __restrict__ part,
+                                                                 const int32_t* __restrict__ ctx_len,
+                                                                 float* __restrict__ o, float* __restrict__ lse,
+                                                                 int B, int Hq, int S_max, int chunk, int nsplit) {
   constexpr int REC = 2 * D + 4;
-  const int bh = blockIdx.x;
-  const int t = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= B * Hq) return;
   const int ctx = dec_len(ctx_len, bh / Hq, S_max);
   float* orow = o + (size_t)bh * D;
   float* lse_out = lse ? lse + bh : nullptr;
   if (ctx == 0) {
-    write_nan_row(orow, lse_out, t);
+    for (int i = lane; i < D; i += 64) orow[i] = __builtin_nanf("");
+    if (lse_out && lane == 0) *lse_out = __builtin_nanf("");
     return;
   }
   const int n = (ctx + chunk - 1) / chunk;
-  merge_records<D>(part + (size_t)bh * nsplit * REC, REC, n, [](int) { return true; }, orow, lse_out);
+  wave_merge<D>(part + (size_t)bh * nsplit * REC, REC, n, [](int) { return true; }, orow, lse_out);
 }
 
-// Balanced schedule: the records of (b, h) sit at slots w + s for the
-// workgroups w whose range meets segment s = b * Hkv + h / G.
+// Balanced schedule: segment s = b * Hkv + h / G covers keys [start, end) of
+// the flattened space; its records sit at slots w + s for the workgroups
+// w = bal_wg(start) .. bal_wg(end - 1).  With fewer keys than workgroups
+// (W < P) some of those ranges are empty and wrote no record.  A wave per head.
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_balanced_kernel(const float* __restrict__ part,
-                                                                  const int32_t* __restrict__ ctx_len,
-                                                                  float* __restrict__ o, float* __restrict__ lse,
-                                                                  int B, int Hq, int Hkv, int S_max, int P) {
+__global__ __launch_bounds__(256) void decode_merge_balanced_kernel(const float* __restrict__ part,
+                                                                    const int32_t* __restrict__ ctx_len,
+                                                                    float* __restrict__ o, float* __restrict__ lse,
+                                                                    int B, int Hq, int Hkv, int S_max, int P) {
   constexpr int REC = 2 * D + 4;
-  __shared__ long long red_ll[2][D / 64];
-  const int bh = blockIdx.x;
-  const int b = bh / Hq, h = bh % Hq;
-  const int Gfull = Hq / Hkv;
-  const int hk = h / Gfull;
-  const int t = threadIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + wave;
+  if (bh >= B * Hq) return;
+  const int b = bh / Hq, h = bh % Hq, Gfull = Hq / Hkv, hk = h / Gfull;
   const int len = dec_len(ctx_len, b, S_max);
   float* orow = o + (size_t)bh * D;
   float* lse_out = lse ? lse + bh : nullptr;
   if (len == 0) {
-    write_nan_row(orow, lse_out, t);
+    for (int i = lane; i < D; i += 64) orow[i] = __builtin_nanf("");
+    if (lse_out && lane == 0) *lse_out = __builtin_nanf("");
     return;
   }
-  // total valid keys and keys before b, block-wide
   long long tot = 0, pre = 0;
-  for (int bb = t; bb < B; bb += D) {
+  for (int bb = lane; bb < B; bb += 64) {
     const int l = dec_len(ctx_len, bb, S_max);
     tot += l;
     if (bb < b) pre += l;
   }
   tot = wave_sum_ll(tot);
   pre = wave_sum_ll(pre);
-  if ((t & 63) == 0) {
-    red_ll[0][t >> 6] = tot;
-    red_ll[1][t >> 6] = pre;
-  }
-  __syncthreads();
-  tot = 0;
-  pre = 0;
-#pragma unroll
-  for (int w = 0; w < D / 64; ++w) {
-    tot += red_ll[0][w];
-    pre += red_ll[1][w];
-  }
   const long long W = tot * Hkv;
   const long long start = pre * Hkv + (long long)hk * len, end = start + len;
-  // workgroup whose range holds `start`
-  long long w = start * P / W;
-  while (w + 1 < P && bal_lo(w + 1, W, P) <= start) ++w;
-  while (w > 0 && bal_lo(w, W, P) > start) --w;
+  const long long w0 = bal_wg(start, W, P);
+  const int n = (int)(bal_wg(end - 1, W, P) - w0 + 1);
   const long long seg = (long long)b * Hkv + hk;
-  // workgroups w .. w+n-1 meet the segment; one with an empty range wrote no record
-  int n = 0;
-  while (w + n < P && bal_lo(w + n, W, P) < end) ++n;
-  const float* rec0 = part + ((size_t)(w + seg) * Gfull + (h % Gfull)) * REC;
-  merge_records<D>(rec0, (size_t)Gfull * REC, n,
-                   [&](int i) { return bal_lo(w + i, W, P) < bal_lo(w + i + 1, W, P); }, orow, lse_out);
+  wave_merge<D>(part + ((size_t)(w0 + seg) * Gfull + (h % Gfull)) * REC, (size_t)Gfull * REC, n,
+                [&](int i) { return W >= P || bal_lo(w0 + i, W, P) < bal_lo(w0 + i + 1, W, P); },
+                orow, lse_out);
 }
 
 template <class Pol, int D, int G>
@@ -798,24 +792,27 @@ hipError_t launch_decode_t(const void* q, const void* rho, const void* kc, const
   hipError_t e;
   if constexpr (sizeof(typename Pol::in_t) == 2) {
     // bf16: 16-column kernel; 16 heads per KV head take two column groups
+#define PLX_P16(GG, HOFF)                                                                          \
+  launch_partial16<D, GG>(q, rho, kc, vc, ctx_len, part, B, Hq, Hkv, S_max, chunk, nsplit, HOFF, \
+                          scale, stream)
     switch (G) {
-      case 1: e = launch_partial16<D, 1>(q, rho, kc, vc, ctx_len, part, B, Hq, Hkv, S_max, chunk, nsplit, 0, scale, stream); break;
-      case 2: e = launch_partial16<D, 2>(q, rho, kc, vc, ctx_len, part, B, Hq, Hkv, S_max, chunk, nsplit, 0, scale, stream); break;
-      case 4: e = launch_partial16<D, 4>(q, rho, kc, vc, ctx_len, part, B, Hq, Hkv, S_max, chunk, nsplit, 0, scale, stream); break;
-      case 8: e = launch_partial16<D, 8>(q, rho, kc, vc, ctx_len, part, B, Hq, Hkv, S_max, chunk, nsplit, 0, scale, stream); break;
+      case 1: e = PLX_P16(1, 0); break;
+      case 2: e = PLX_P16(2, 0); break;
+      case 4: e = PLX_P16(4, 0); break;
+      case 8: e = PLX_P16(8, 0); break;
       default:
-        e = launch_partial16<D, 8>(q, rho, kc, vc, ctx_len, part, B, Hq, Hkv, S_max, chunk, nsplit, 0, scale, stream);
-        if (e == hipSuccess)
-          e = launch_partial16<D, 8>(q, rho, kc, vc, ctx_len, part, B, Hq, Hkv, S_max, chunk, nsplit, 8, scale, stream);
+        e = PLX_P16(8, 0);
+        if (e == hipSuccess) e = PLX_P16(8, 8);
         break;
     }
+#undef PLX_P16
     if (e != hipSuccess) return e;
     if (chunk <= 0)
-      hipLaunchKernelGGL((decode_merge_balanced_kernel<D>), dim3(B * Hq), dim3(D), 0, stream, part,
-                         ctx_len, o, lse, B, Hq, Hkv, S_max, nsplit);
+      hipLaunchKernelGGL((decode_merge_balanced_kernel<D>), dim3((B * Hq + 3) / 4), dim3(256), 0, stream,
+                         part, ctx_len, o, lse, B, Hq, Hkv, S_max, nsplit);
     else
-      hipLaunchKernelGGL((decode_merge_chunk_kernel<D>), dim3(B * Hq), dim3(D), 0, stream, part,
-                         ctx_len, o, lse, Hq, S_max, chunk, nsplit);
+      hipLaunchKernelGGL((decode_merge_chunk_kernel<D>), dim3((B * Hq + 3) / 4), dim3(256), 0, stream,
+                         part, ctx_len, o, lse, B, Hq, S_max, chunk, nsplit);
     return hipGetLastError();
   } else {
     // fp32: the generic 32-column kernel (chunked schedule only)
@@ -827,8 +824,8 @@ hipError_t launch_decode_t(const void* q, const void* rho, const void* kc, const
       default: e = launch_partial<Pol, D, 16>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_chunk_kernel<D>), dim3(B * Hq), dim3(D), 0, stream, part, ctx_len,
-                       o, lse, Hq, S_max, chunk, nsplit);
+    hipLaunchKernelGGL((decode_merge_chunk_kernel<D>), dim3((B * Hq + 3) / 4), dim3(256), 0, stream,
+                       part, ctx_len, o, lse, B, Hq, S_max, chunk, nsplit);
     return hipGetLastError();
   }
 }

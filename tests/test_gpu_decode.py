@@ -126,6 +126,49 @@ def test_bf16_balanced_schedule_many_short_sequences(gpu_lib, Hq, Hkv):
     assert np.max(np.abs(o - o_split)) < 1e-3
 
 
+@pytest.mark.parametrize("Hq,Hkv,S,ctx_list,bad", [
+    (4, 2, 4096, [3, 9, 5, 1, 7, 2], {1: 0, 4: 4097}),   # fewer keys than workgroups
+    (16, 1, 8192, [7, 2, 11], {1: -5}),                 # two 8-head passes, sparse
+])
+def test_bf16_balanced_schedule_fewer_keys_than_workgroups(gpu_lib, Hq, Hkv, S, ctx_list, bad):
+    """Automatic schedule when the valid keys number fewer than the workgroups:
+    ranges hold at most one key, some are empty, and the workgroup that
+    completes a segment's count merges it."""
+    import torch
+
+    B, d = len(ctx_list), 128
+    say(f"case decode bf16 balanced sparse B{B} Hq{Hq} Hkv{Hkv} S{S} ctx {ctx_list} invalid {bad}")
+    wl = inputs.make_decode(B, Hq, Hkv, d, 0, S_max=S, dtype="bf16", seed=86, ctx_list=ctx_list)
+    t = _dev(wl)
+    ctx = wl.ctx_len.copy()
+    for b, c in bad.items():
+        ctx[b] = c
+    t["ctx"] = torch.from_numpy(ctx).cuda()
+    got = _run(wl, 0, t)
+    for b in bad:
+        assert np.all(np.isnan(got["o"][b])) and np.all(np.isnan(got["lse"][b]))
+    heads = [(b, h) for b in range(B) if b not in bad for h in range(Hq)]
+    ref = _oracle(wl, heads)
+    check_bf16(np.array([got["o"][b, h] for b, h in heads]), ref["o"], "o")
+    assert np.max(np.abs(np.array([got["lse"][b, h] for b, h in heads]) - ref["lse"])) <= LSE_ABS
+
+
+@pytest.mark.parametrize("Hq,Hkv,S", [(16, 1, 65536), (2, 1, 200000)])
+def test_bf16_balanced_schedule_one_long_segment(gpu_lib, Hq, Hkv, S):
+    """One sequence spread over every workgroup: a segment merges 64 and more
+    records (the merge's multi-batch path), with one or two head passes."""
+    B, d = 1, 128
+    say(f"case decode bf16 balanced one segment B{B} Hq{Hq} Hkv{Hkv} ctx{S}")
+    wl = inputs.make_decode(B, Hq, Hkv, d, S, dtype="bf16", seed=87)
+    got = _run(wl)
+    heads = [(0, h) for h in range(Hq)]
+    ref = _oracle(wl, heads)
+    check_bf16(np.array([got["o"][b, h] for b, h in heads]), ref["o"], "o")
+    assert np.max(np.abs(np.array([got["lse"][b, h] for b, h in heads]) - ref["lse"])) <= LSE_ABS
+    split = _run(wl, 5)
+    assert np.max(np.abs(got["o"] - split["o"])) < 1e-3
+
+
 def test_decode_matches_prefill_last_row(gpu_lib):
     """Decode over the first t cache rows equals the prefill output at row t-1
     (both on the GPU, both checked against the oracle)."""
