@@ -28,6 +28,10 @@
  *     bf16 MFMA with fp32 accumulation, softmax-weighted GEMMs with fp16 operands
  *     and fp32 accumulation) or PLX_F32 (fp32 throughout).  Every output (o, LSE,
  *     auxiliaries, gradients) is fp32.
+ *   - bf16 inputs that feed fp16 operands (v in every call; q, rho, dO and k as
+ *     well in plx_bwd) must lie within fp16's range, |x| <= 65504: the
+ *     conversion is exact down to 2^-14 and rounds smaller magnitudes to fp16's
+ *     subnormal grid (absolute error <= 2^-25); larger ones become infinite.
  *   - Supported head dims: d = 64 or 128 (d_k = d_v = d).
  *   - All pointers are DEVICE pointers unless stated.  The caller owns every
  *     buffer; the library never allocates or frees device memory and keeps no
@@ -101,10 +105,11 @@ plx_status plx_fwd_prefill(const void* q, const void* k, const void* v, const vo
  * Query (b, h) attends to the cache rows [0, ctx_len[b]) of KV head h/(Hq/Hkv)
  * (the cache already holds the current token; no mask).  The keys are cut into
  * ranges processed by separate workgroups, each producing a partial record
- * (m, l, C, O, U) -- running max, sum of P, sum of P . R, P V and (P . R) V --
- * which a second kernel merges:
- *   M = max m_s, a_s = exp(m_s - M), l = sum a_s l_s, C/O/U likewise,
- *   o = (O/l)(1 + C/l) - U/l,   LSE = M + ln l.
+ * (m, l, e, C, O, U) -- running max, sum of P as the value GEMMs used it, sum
+ * of the unrounded p, sum of P . R, P V and (P . R) V -- which a second kernel
+ * merges:
+ *   M = max m_s, a_s = exp(m_s - M), l = sum a_s l_s, e/C/O/U likewise,
+ *   o = (O/l)(1 + C/l) - U/l,   LSE = M + ln e.
  * C/l equals kbar . rho (kbar = P K / l), the only use the output makes of the
  * mean key, so the record carries that scalar instead of the vector P K.
  *
