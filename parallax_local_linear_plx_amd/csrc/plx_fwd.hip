@@ -33,6 +33,7 @@ constexpr int FWD_BR = 128;
 constexpr int FWD_BC = 64;
 constexpr int FWD_THREADS = 256;
 constexpr int FWD16_WAVES = 8;  // waves per workgroup of the bf16 kernel
+constexpr int F16_BC = 128;     // keys per LDS tile of the bf16 kernel
 // Lazy-rescale threshold (log2 units): p stays <= 16, so the fp16 operand
 // p * r overflows only for |r| = |rho . k| > 4094.
 constexpr float kRescaleLog2 = 4.f;
@@ -466,22 +467,40 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
 //     is the column sum over the keys of the rounded P / P.R);
 //   [O|U]^T += V^T [P | P.R]^T: D/16 d tiles, A = V^T from ds_read_b64_tr_b16,
 //     element e of group g is key 16 (e / 4) + 4 g + e % 4, matching P's order.
-// Workgroup: 8 waves, 128 query rows of one (b, h).  Tiles of 64 keys are
-// triple-buffered in LDS (K bf16 rows, V fp16 rows), with the global loads
-// issued two tiles ahead into alternating register sets: one barrier per tile.
+// The K operands of a sub-tile are all read from LDS before its first score
+// MFMA, and the V operands before its softmax, so that their latency is paid
+// once per sub-tile and overlaps the softmax.
+// Workgroup: 8 waves, 128 query rows of one (b, h).  Tiles of 128 keys are
+// double-buffered in LDS (K bf16 rows, V fp16 rows); the global loads of tile
+// j+1 are issued at the start of tile j and stored at its end, before the
+// tile's single barrier.
 template <int D>
 struct Fwd16Smem {
   // row strides (elements), chosen so that the ds_read_b128 of K and the
   // transpose reads of V are free of bank conflicts (measured)
   static constexpr int KLD = D + 16;
   static constexpr int VLD = D + 16;
-  alignas(16) uint16_t k[3][FWD_BC * KLD];
-  alignas(16) _Float16 v[3][FWD_BC * VLD];
+  alignas(16) uint16_t k[2][F16_BC * KLD];
+  alignas(16) _Float16 v[2][F16_BC * VLD];
 };
 
 __device__ __forceinline__ f16x4 tr16_f16(const _Float16* p) {
   s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
   return __builtin_bit_cast(f16x4, t);
+}
+
+// LDS byte address of a shared-memory pointer, and transpose / 16-byte reads
+// at such an address.  A base address the compiler cannot see through keeps
+// every per-read displacement in the instruction's offset field.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)((__attribute__((address_space(3))) const char*)p);
+}
+__device__ __forceinline__ f16x4 tr16_at(unsigned a) {
+  s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(size_t)a);
+  return __builtin_bit_cast(f16x4, t);
+}
+__device__ __forceinline__ u32x4 ld128_at(unsigned a) {
+  return *(__attribute__((address_space(3))) const u32x4*)(size_t)a;
 }
 
 template <int D, int NW>
@@ -495,7 +514,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
   constexpr int NS = D / 32;        // score MFMA steps over d
   constexpr int ND = D / 16;        // 16-row d tiles of O^T / U^T
   constexpr int CPR = D / 8;        // 16-byte chunks per row
-  constexpr int NCH = FWD_BC * CPR / NT;  // chunks per thread per tile
+  constexpr int NCH = F16_BC * CPR / NT;  // chunks per thread per tile
   using SM = Fwd16Smem<D>;
   __shared__ SM sm;
 
@@ -520,15 +539,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
   const uint16_t* vp = v + ((size_t)(b * Hkv + hk) * T) * D;
 
   const int kend = min(T, q0 + BR);
-  const int ntiles = (kend + FWD_BC - 1) / FWD_BC;
+  const int ntiles = (kend + F16_BC - 1) / F16_BC;
   // 32-key sub-tiles this wave attends to: keys [0, min(kend, qw + 16))
   const int nsub = (min(kend, qw + 16) + 31) / 32;
 
   // global -> register prefetch of one K / V tile (rows past T read row T-1:
   // finite, and masked by the causal test since they follow every query)
   struct Pre { u32x4 k[NCH], v[NCH]; };
-  Pre preA, preB;
+  Pre preA;
   auto gload = [&](Pre& p, int key0) {
+    if (key0 + F16_BC <= T) {
+      // whole tile in range: scalar tile base plus this thread's fixed offsets
+      const uint16_t* kt = kp + (size_t)key0 * D;
+      const uint16_t* vt = vp + (size_t)key0 * D;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int off = (threadIdx.x + NT * i) * 8;  // row * D + column
+        p.k[i] = *reinterpret_cast<const u32x4*>(kt + off);
+        p.v[i] = *reinterpret_cast<const u32x4*>(vt + off);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int it = threadIdx.x + NT * i;
@@ -566,7 +597,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     rop[s] = __builtin_bit_cast(bf16x8, ra);
   }
   lds_put(preA, 0);
-  if (ntiles > 1) gload(preB, FWD_BC);
   __syncthreads();
 
   f32x4 oacc[ND], uacc[ND];
@@ -581,6 +611,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
   f16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.f;
+  asm volatile("" : "+v"(ones));  // kept in registers, not rebuilt per sub-tile
   // e_part: this lane's unrounded sum of p (the LSE only)
   float m_run = -INFINITY, e_part = 0.f;
 
@@ -588,12 +619,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     // scores
     __builtin_amdgcn_s_setprio(1);
     f32x4 sacc[2], racc[2];
+    unsigned kaddr = lds_addr(&sm.k[kbuf][(32 * st + c) * SM::KLD + 8 * g]);
+    asm volatile("" : "+v"(kaddr));
+    // every K operand of the sub-tile in flight before the first MFMA
+    bf16x8 ka[2][NS];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        ka[t][s] = __builtin_bit_cast(bf16x8, ld128_at(kaddr + 2 * (16 * t * SM::KLD + 32 * s)));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint16_t* krow = &sm.k[kbuf][(32 * st + 16 * t + c) * SM::KLD + 8 * g];
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + 32 * s));
+        const bf16x8 a = ka[t][s];
         const f32x4 zs = s == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : sacc[t];
         const f32x4 zr = s == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : racc[t];
         sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[s], zs, 0, 0, 0);
@@ -601,6 +641,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
       }
     }
     __builtin_amdgcn_s_setprio(0);
+    // V^T operands of the value MFMAs, in flight during the softmax
+    unsigned vaddr = lds_addr(&sm.v[vbuf][(32 * st + 4 * g + (c >> 2)) * SM::VLD + 4 * (c & 3)]);
+    asm volatile("" : "+v"(vaddr));
+    f16x4 va[ND][2];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      va[dt][0] = tr16_at(vaddr + 2 * 16 * dt);
+      va[dt][1] = tr16_at(vaddr + 2 * (16 * dt + 16 * SM::VLD));
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // causal mask where the sub-tile reaches past the wave's first query
     if (kbase + 31 > qw) {
 #pragma unroll
@@ -616,10 +666,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
       for (int j = 0; j < 4; ++j) mt = fmaxf(mt, sacc[t][j]);
     {
       // max over the four 16-lane groups: permlane swaps, no LDS round trip
+      // (NaN-propagating maximum: no canonicalising moves around the swaps)
       const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-      mt = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+      mt = __builtin_elementwise_maximum(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
       const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-      mt = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+      mt = __builtin_elementwise_maximum(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
     }
     mt *= scale_log2;
     // lazy rescale: the reference max moves only when a row's max exceeds it
@@ -662,10 +713,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop, lacc, 0, 0, 0);
     cacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, prop, cacc, 0, 0, 0);
     // value MFMAs
-    const _Float16* vt = &sm.v[vbuf][(32 * st + 4 * g + (c >> 2)) * SM::VLD + 4 * (c & 3)];
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
-      const f16x4 v0 = tr16_f16(vt + 16 * dt), v1 = tr16_f16(vt + 16 * dt + 16 * SM::VLD);
+      const f16x4 v0 = va[dt][0], v1 = va[dt][1];
       f16x8 av;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -678,21 +728,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // Tile j lives in buffer j % 3.  Iteration j issues the global loads of
-  // tile j+2 (register set j % 2) and stores tile j+1 (set (j+1) % 2, issued
-  // an iteration earlier) into buffer (j+1) % 3, last read in iteration j-2.
-  auto iter = [&](int j, Pre& issue, Pre& store) {
-    const int key0 = j * FWD_BC;
-    if (j + 2 < ntiles) gload(issue, key0 + 2 * FWD_BC);
-    const int buf = j % 3;
-    if (2 * j < nsub) subtile(buf, buf, 0, key0);
-    if (2 * j + 1 < nsub) subtile(buf, buf, 1, key0 + 32);
-    if (j + 1 < ntiles) lds_put(store, (j + 1) % 3);
+  // Tile j lives in buffer j % 2.  Iteration j issues the global loads of
+  // tile j+1 and stores them into the other buffer, whose tile j-1 every wave
+  // finished reading before the barrier that ended iteration j-1.
+  auto iter = [&](int j, int buf) {
+    const int key0 = j * F16_BC;
+    if (j + 1 < ntiles) gload(preA, key0 + F16_BC);
+#pragma unroll
+    for (int st = 0; st < F16_BC / 32; ++st)
+      if (4 * j + st < nsub) subtile(buf, buf, st, key0 + 32 * st);
+    if (j + 1 < ntiles) lds_put(preA, buf ^ 1);
     __syncthreads();
   };
   for (int j = 0; j < ntiles; j += 2) {
-    iter(j, preA, preB);
-    if (j + 1 < ntiles) iter(j + 1, preB, preA);
+    iter(j, 0);
+    if (j + 1 < ntiles) iter(j + 1, 1);
   }
 
   // epilogue: o = (O/l)(1 + C/l) - U/l; LSE = ln sum exp(scaled scores)
