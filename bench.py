@@ -15,7 +15,7 @@ synchronisations.  The CPU baseline is the fp64 oracle on a bounded sample of
 prefill rows, timed on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
-                       [--only all|prefill|decode|decode_long|train|copy] [--no-cpu] [--no-graph]
+                       [--only all|prefill|decode|decode_long|train|copy|decode_sweep] [--no-cpu] [--no-graph]
 """
 
 from __future__ import annotations
@@ -144,6 +144,60 @@ def bench_decode(steps, warmup, B, ctx_len, S_max, name, seed, graph=True):
             "GB/s_graph10": (kv_bytes + io_bytes) / (ms_graph * 1e-3) / 1e9 if graph else None,
             "flop_per_byte": flops / (kv_bytes + io_bytes),
             "ctx_len_sum": int(np.sum(ctx_len))}
+
+
+# ------------------------------------------------------------ decode sweep
+SWEEP_BATCH = (1, 4, 16, 64, 128)
+SWEEP_CTX = (1024, 4096, 16384, 65536, 131072)
+SWEEP_MAX_KEYS = 1 << 22  # B * ctx cap: 17 GB of K and V
+
+
+def bench_decode_sweep(steps, warmup):
+    """Decode latency over batch x context (uniform lengths), automatic schedule.
+    One K/V buffer sized for the largest cell is filled once and viewed per cell."""
+    import torch
+
+    from parallax_local_linear_plx_amd import decode_workspace_size, plx_decode
+
+    Hq, Hkv, d = 16, 8, 128
+    n = SWEEP_MAX_KEYS * Hkv * d
+    g = torch.Generator(device="cuda")
+    g.manual_seed(51)
+    kv = []
+    for _ in range(2):
+        buf = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        chunk = 1 << 26
+        for i in range(0, n, chunk):
+            m = min(chunk, n - i)
+            buf[i:i + m] = torch.randn(m, generator=g, device="cuda").to(torch.bfloat16)
+        kv.append(buf)
+    cells = []
+    for B in SWEEP_BATCH:
+        for ctx in SWEEP_CTX:
+            if B * ctx > SWEEP_MAX_KEYS:
+                continue
+            kc = kv[0][:B * Hkv * ctx * d].view(B, Hkv, ctx, d)
+            vc = kv[1][:B * Hkv * ctx * d].view(B, Hkv, ctx, d)
+            q = torch.randn(B, Hq, d, generator=g, device="cuda").to(torch.bfloat16)
+            rho = (0.1 * torch.randn(B, Hq, d, generator=g, device="cuda")).to(torch.bfloat16)
+            cl = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+            o = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+            ws = torch.empty(decode_workspace_size(B, Hq, Hkv, ctx, d, 0), dtype=torch.uint8, device="cuda")
+
+            def step():
+                plx_decode(q, rho, kc, vc, cl, num_splits=0, workspace=ws, o=o, lse=False)
+
+            # warm up for >= 50 ms whatever the cell's size: the clocks ramp
+            # only under sustained work
+            est = time_steps(step, 5, 2)
+            ms = time_steps(step, steps, max(warmup, int(50.0 / max(est, 1e-3))))
+            nbytes = B * Hkv * ctx * d * 2 * 2 + B * Hq * d * (2 + 2 + 4)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            cells.append({"B": B, "ctx": ctx, "us_per_step": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                          "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
+            log(f"  B={B:4d} ctx={ctx:7d}: {ms * 1e3:9.1f} us  {gbs:7.0f} GB/s  ({gbs / PEAK_HBM_GBS:.1%})")
+    return {"workload": "bf16 decode sweep Hq=16 Hkv=8 d=128, uniform ctx, automatic schedule",
+            "cells": cells}
 
 
 # ------------------------------------------------------------------ training
@@ -281,7 +335,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--only", default="all",
-                    choices=["all", "prefill", "decode", "decode_long", "train", "copy"])
+                    choices=["all", "prefill", "decode", "decode_long", "train", "copy", "decode_sweep"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay decode timing")
     args = ap.parse_args()
@@ -307,6 +361,13 @@ def main():
         log(f"  {res['prefill']['ms'] * 1e3:.1f} us  {res['prefill']['tflops']:.1f} TFLOP/s")
     if args.only == "copy":
         print(json.dumps(bench_copy(args.steps)), flush=True)
+        return
+    if args.only == "decode_sweep":
+        log("decode sweep (batch x context) ...")
+        sweep = bench_decode_sweep(max(10, args.steps // 2), max(10, args.warmup // 3))
+        print(json.dumps({"metric": "decode us/step and HBM GB/s over batch x context", "n_gpus": 1,
+                          "higher_is_better": False, "unit": "us/step", "dtype": "bf16",
+                          "data": "synthetic", "decode_sweep": sweep}), flush=True)
         return
     if args.only in ("all", "decode"):
         log("decode B64 ctx8192 ...")
