@@ -513,6 +513,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq16_kernel(
   const float ci = qvalid ? c_aux[rowbase + my_q] : 0.f;
   const float Gi = qvalid ? Gv[rowbase + my_q] : 0.f;
   const float di = qvalid ? dlt[rowbase + my_q] : 0.f;
+  // dS = p [(1 + c - r) A - G + delta (r - c)] = p [A k1 + r (delta - A) - k2]
+  const float k1 = 1.f + ci, k2 = Gi + di * ci;
   lds_put(0);
   __syncthreads();
 
@@ -528,43 +530,35 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq16_kernel(
     const int buf = j & 1;
     if (j + 1 < ntiles) gload(key0 + DQ_BC);
     if (key0 <= qw + 31) {
-      f32x16 sa[2], ra[2], aa[2];
+      // rows past T hold zero operands and are never stored, so only the
+      // causal edge needs a mask
+      const bool diag = key0 + DQ_BC - 1 > qw;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        sa[st] = ra[st] = aa[st] = zero16();
+        f32x16 sa = zero16(), ra = zero16(), aa = zero16();
         const _Float16* krow = &ks[buf][(32 * st + col) * LD + 8 * half];
         const _Float16* vrow = &vs[buf][(32 * st + col) * LD + 8 * half];
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const f16x8 ak = *reinterpret_cast<const f16x8*>(krow + 16 * s);
           const f16x8 av = *reinterpret_cast<const f16x8*>(vrow + 16 * s);
-          sa[st] = mma16(ak, qop[s], sa[st]);
-          ra[st] = mma16(ak, rop[s], ra[st]);
-          aa[st] = mma16(av, gop[s], aa[st]);
+          sa = mma16(ak, qop[s], sa);
+          ra = mma16(ak, rop[s], ra);
+          aa = mma16(av, gop[s], aa);
         }
-      }
-      // dS^T and dR^T in place of S^T and R^T
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int a = 0; a < 16; ++a) {
-          const int key = key0 + 32 * st + acc_row(a, half);
-          float p = fast_exp2(__builtin_fmaf(sa[st][a], scale_log2, -lse2));
-          if (key > my_q || !qvalid) p = 0.f;
-          const float r = ra[st][a], A = aa[st][a];
-          const float f = 1.f + ci - r;
-          sa[st][a] = p * (f * A - Gi + di * (r - ci));
-          ra[st][a] = -p * (A - di);
-        }
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
+          // dS^T and dR^T of 8 keys, straight into the fp16 operands
           f16x8 dsop, drop;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            dsop[e] = (_Float16)sa[st][8 * s + e];
-            drop[e] = (_Float16)ra[st][8 * s + e];
+            const int a = 8 * s + e;
+            float p = fast_exp2(__builtin_fmaf(sa[a], scale_log2, -lse2));
+            if (diag && key0 + 32 * st + acc_row(a, half) > my_q) p = 0.f;
+            const float r = ra[a], A = aa[a];
+            const float t = di - A;
+            dsop[e] = (_Float16)(p * __builtin_fmaf(A, k1, __builtin_fmaf(r, t, -k2)));
+            drop[e] = (_Float16)(p * t);
           }
 #pragma unroll
           for (int dt = 0; dt < ND; ++dt) {
@@ -573,6 +567,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq16_kernel(
             dra[dt] = mma16(a, drop, dra[dt]);
           }
         }
+      }
     }
     if (j + 1 < ntiles) lds_put((j + 1) & 1);  // buffer last read in iteration j-1
     __syncthreads();
@@ -615,7 +610,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv16_kernel(
   __shared__ alignas(16) _Float16 qs_[2][BQ * LD];
   __shared__ alignas(16) _Float16 rs_[2][BQ * LD];
   __shared__ alignas(16) _Float16 gs_[2][BQ * LD];
-  __shared__ alignas(16) float sc_[2][4][BQ];  // lse * log2e, c, G, delta
+  __shared__ alignas(16) float sc_[2][4][BQ];  // lse * log2e, 1 + c, G + delta c, delta
 
   const int bhk_count = B * Hkv;
   const int lin = blockIdx.x;
@@ -656,7 +651,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv16_kernel(
     }
     if (threadIdx.x < BQ) {
       const size_t r = rowbase + min(qt0 + (int)threadIdx.x, T - 1);
-      psc[0] = lse[r] * kLog2e;
+      psc[0] = lse[r];
       psc[1] = c_aux[r];
       psc[2] = Gv[r];
       psc[3] = dlt[r];
@@ -672,8 +667,11 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv16_kernel(
       *reinterpret_cast<f16x8*>(&gs_[buf][o]) = cvt_bf16x8_f16(pg[i]);
     }
     if (threadIdx.x < BQ) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) sc_[buf][m][threadIdx.x] = psc[m];
+      // per query row: lse * log2e, k1 = 1 + c, k2 = G + delta c, delta
+      sc_[buf][0][threadIdx.x] = psc[0] * kLog2e;
+      sc_[buf][1][threadIdx.x] = 1.f + psc[1];
+      sc_[buf][2][threadIdx.x] = psc[2] + psc[3] * psc[1];
+      sc_[buf][3][threadIdx.x] = psc[3];
     }
   };
 
@@ -720,36 +718,33 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv16_kernel(
         ra = mma16(*reinterpret_cast<const f16x8*>(rrow + 16 * s), kop[s], ra);
         aa = mma16(*reinterpret_cast<const f16x8*>(grow + 16 * s), vop[s], aa);
       }
-      // lane column = key my_k; accumulator slot a = query qs + acc_row(a, half)
-      float pt[16], ds[16], dr[16];
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int r0 = 32 * st + 8 * i4 + 4 * half;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sc_[buf][0][r0]);
-        const f32x4 c4 = *reinterpret_cast<const f32x4*>(&sc_[buf][1][r0]);
-        const f32x4 g4 = *reinterpret_cast<const f32x4*>(&sc_[buf][2][r0]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sc_[buf][3][r0]);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int a = 4 * i4 + jj;
-          const int qi = qt0 + r0 + jj;
-          float p = fast_exp2(__builtin_fmaf(sa[a], scale_log2, -l4[jj]));
-          if (qi < my_k || qi >= T) p = 0.f;
-          const float r = ra[a], A = aa[a];
-          const float f = 1.f + c4[jj] - r;
-          pt[a] = p * f;
-          ds[a] = scale * p * (f * A - g4[jj] + d4[jj] * (r - c4[jj]));
-          dr[a] = -p * (A - d4[jj]);
-        }
-      }
+      // lane column = key my_k; accumulator slot a = query qs + acc_row(a, half).
+      // Masked: queries before the key (the diagonal sub-tile) and rows past T.
+      const bool edge = qs < kw + 31 || qs + 31 >= T;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         f16x8 pop, dsop, drop;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pop[e] = (_Float16)pt[8 * s + e];
-          dsop[e] = (_Float16)ds[8 * s + e];
-          drop[e] = (_Float16)dr[8 * s + e];
+        for (int i4 = 0; i4 < 2; ++i4) {
+          const int r0 = 32 * st + 8 * (2 * s + i4) + 4 * half;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sc_[buf][0][r0]);
+          const f32x4 k14 = *reinterpret_cast<const f32x4*>(&sc_[buf][1][r0]);
+          const f32x4 k24 = *reinterpret_cast<const f32x4*>(&sc_[buf][2][r0]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sc_[buf][3][r0]);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int a = 8 * s + 4 * i4 + jj, e = 4 * i4 + jj;
+            float p = fast_exp2(__builtin_fmaf(sa[a], scale_log2, -l4[jj]));
+            if (edge) {
+              const int qi = qt0 + r0 + jj;
+              if (qi < my_k || qi >= T) p = 0.f;
+            }
+            const float r = ra[a], A = aa[a];
+            const float t = d4[jj] - A;
+            pop[e] = (_Float16)(p * (k14[jj] - r));
+            dsop[e] = (_Float16)((scale * p) * __builtin_fmaf(A, k14[jj], __builtin_fmaf(r, t, -k24[jj])));
+            drop[e] = (_Float16)(p * t);
+          }
         }
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
