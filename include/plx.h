@@ -157,7 +157,10 @@ plx_status plx_decode(const void* q, const void* rho, const void* k_cache, const
  *   vbar_aux    [B, Hq, T, d]  fp32 (forward auxiliary, required)
  *   dq, drho    [B, Hq, T, d]  fp32, written (overwritten, not accumulated)
  *   dk, dv      [B, Hkv, T, d] fp32, written (overwritten, not accumulated)
- *   workspace   at least plx_bwd_workspace_size(...) bytes, 16-byte aligned
+ *   workspace   at least plx_bwd_workspace_size(...) bytes, 16-byte aligned:
+ *               G_i = dO_i . o_i and delta_i (fp32 per query row), then, used by
+ *               the bf16 path, fp16 copies of q, rho, dO, k and v (one
+ *               conversion pass, so that the main kernels read fp16 operands)
  * The result is deterministic (no atomics): one kernel owns each key block and
  * one kernel owns each query block.
  */

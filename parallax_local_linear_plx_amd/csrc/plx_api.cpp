@@ -100,8 +100,9 @@ plx_status plx_decode(const void* q, const void* rho, const void* k_cache, const
 size_t plx_bwd_workspace_size(int B, int Hq, int Hkv, int T, int d) {
   if (B < 1 || Hq < 1 || Hkv < 1 || T < 1) return 0;
   if (d != 64 && d != 128) return 0;
-  // G_i = dO_i . o_i and delta_i = dO_i . vbar_i, fp32 each
-  return (size_t)2 * B * Hq * T * sizeof(float);
+  // G_i = dO_i . o_i and delta_i = dO_i . vbar_i (fp32 each), then the fp16
+  // copies of q, rho, dO, k and v that the bf16 path's kernels read
+  return plx::bwd_workspace_bytes(B, Hq, Hkv, T, d);
 }
 
 plx_status plx_bwd(const void* q, const void* k, const void* v, const void* rho, const void* d_o,

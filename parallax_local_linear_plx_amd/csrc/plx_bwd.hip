@@ -18,6 +18,8 @@
 //   dkdv  : key-outer: one key per lane column (S = Q K^T), loops over the
 //           query tiles of every head that shares the KV head, accumulates
 //           dV^T = dO^T Ptilde and dK^T = Q^T (tau dS) + rho^T dR.
+#include <algorithm>
+
 #include "plx_common.hpp"
 #include "plx_kernels.hpp"
 
@@ -400,6 +402,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv_kernel(
 // top of an iteration, converted and stored at its end (into the buffer read
 // one iteration earlier), followed by the iteration's single barrier.
 // Rows past T are loaded as row T-1 (finite) and given p = 0.
+inline size_t bwd_ws_align(size_t n) { return (n + 255) & ~(size_t)255; }
 constexpr int B16_LD = 24;  // row padding (halves): ds_read_b128 rows and transpose reads spread over the banks
 
 __device__ __forceinline__ f16x4 tr_read(const _Float16* p) {
@@ -434,11 +437,21 @@ __device__ __forceinline__ f16x8 cvt_bf16x8_f16(u32x4 raw) {
   return h;
 }
 
+// bf16 -> fp16 copy of n8 chunks of 8 elements: the bf16 backward reads its
+// MFMA operands (q, rho, dO, K, V) from these copies, so the main kernels stage
+// tiles without converting them again for every workgroup that reads them.
+__global__ __launch_bounds__(256) void cvt_f16_kernel(const u32x4* __restrict__ src, f16x8* __restrict__ dst,
+                                                     long long n8) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long long)gridDim.x * 256)
+    dst[i] = cvt_bf16x8_f16(src[i]);
+}
+
 __device__ __forceinline__ f32x16 mma16(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// dQ and drho, query-outer (bf16).
+// dQ and drho, query-outer (bf16 inputs; q, k, v, rho and dO point to their
+// fp16 copies).
 template <int D>
 __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -489,8 +502,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq16_kernel(
     for (int i = 0; i < NCH; ++i) {
       const int it = threadIdx.x + BWD_THREADS * i;
       const int o = (it / CPR) * LD + (it % CPR) * 8;
-      *reinterpret_cast<f16x8*>(&ks[buf][o]) = cvt_bf16x8_f16(pk[i]);
-      *reinterpret_cast<f16x8*>(&vs[buf][o]) = cvt_bf16x8_f16(pv[i]);
+      *reinterpret_cast<f16x8*>(&ks[buf][o]) = __builtin_bit_cast(f16x8, pk[i]);
+      *reinterpret_cast<f16x8*>(&vs[buf][o]) = __builtin_bit_cast(f16x8, pv[i]);
     }
   };
 
@@ -505,9 +518,9 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq16_kernel(
       ra = *reinterpret_cast<const u32x4*>(rho + off);
       ga = *reinterpret_cast<const u32x4*>(d_o + off);
     }
-    qop[s] = cvt_bf16x8_f16(qa);
-    rop[s] = cvt_bf16x8_f16(ra);
-    gop[s] = cvt_bf16x8_f16(ga);
+    qop[s] = __builtin_bit_cast(f16x8, qa);
+    rop[s] = __builtin_bit_cast(f16x8, ra);
+    gop[s] = __builtin_bit_cast(f16x8, ga);
   }
   const float lse2 = qvalid ? lse[rowbase + my_q] * kLog2e : 0.f;
   const float ci = qvalid ? c_aux[rowbase + my_q] : 0.f;
@@ -593,8 +606,9 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq16_kernel(
   }
 }
 
-// dK and dV, key-outer (bf16): the query tiles of all G heads of the KV head
-// form one sequence, prefetched one tile ahead.
+// dK and dV, key-outer (bf16 inputs, read from their fp16 copies): the query
+// tiles of all G heads of the KV head form one sequence, prefetched one tile
+// ahead.
 template <int D>
 __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -662,9 +676,9 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv16_kernel(
     for (int i = 0; i < NCH; ++i) {
       const int it = threadIdx.x + BWD_THREADS * i;
       const int o = (it / CPR) * LD + (it % CPR) * 8;
-      *reinterpret_cast<f16x8*>(&qs_[buf][o]) = cvt_bf16x8_f16(pq[i]);
-      *reinterpret_cast<f16x8*>(&rs_[buf][o]) = cvt_bf16x8_f16(pr[i]);
-      *reinterpret_cast<f16x8*>(&gs_[buf][o]) = cvt_bf16x8_f16(pg[i]);
+      *reinterpret_cast<f16x8*>(&qs_[buf][o]) = __builtin_bit_cast(f16x8, pq[i]);
+      *reinterpret_cast<f16x8*>(&rs_[buf][o]) = __builtin_bit_cast(f16x8, pr[i]);
+      *reinterpret_cast<f16x8*>(&gs_[buf][o]) = __builtin_bit_cast(f16x8, pg[i]);
     }
     if (threadIdx.x < BQ) {
       // per query row: lse * log2e, k1 = 1 + c, k2 = G + delta c, delta
@@ -685,8 +699,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv16_kernel(
       ka = *reinterpret_cast<const u32x4*>(k + off);
       va = *reinterpret_cast<const u32x4*>(v + off);
     }
-    kop[s] = cvt_bf16x8_f16(ka);
-    vop[s] = cvt_bf16x8_f16(va);
+    kop[s] = __builtin_bit_cast(f16x8, ka);
+    vop[s] = __builtin_bit_cast(f16x8, va);
   }
   lds_put(0);
   __syncthreads();
@@ -797,15 +811,30 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   const int nqb = (T + DQ_BR - 1) / DQ_BR;
   const int nkb = (T + KV_BK - 1) / KV_BK;
   if constexpr (sizeof(in_t) == 2) {
+    // fp16 copies of the five inputs follow G and delta in the workspace
+    const size_t nq = (size_t)rows * D, nk = (size_t)B * Hkv * T * D;
+    uint16_t* h = (uint16_t*)((char*)ws + bwd_ws_align(2 * rows * sizeof(float)));
+    uint16_t* q16 = h;
+    uint16_t* r16 = q16 + nq;
+    uint16_t* g16 = r16 + nq;
+    uint16_t* k16 = g16 + nq;
+    uint16_t* v16 = k16 + nk;
+    const void* src[5] = {q, rho, d_o, k, v};
+    uint16_t* dst[5] = {q16, r16, g16, k16, v16};
+    for (int i = 0; i < 5; ++i) {
+      const long long n8 = (long long)(i < 3 ? nq : nk) / 8;
+      const unsigned blocks = (unsigned)std::min<long long>((n8 + 255) / 256, 8192);
+      hipLaunchKernelGGL(cvt_f16_kernel, dim3(blocks), dim3(256), 0, stream, (const u32x4*)src[i],
+                         (f16x8*)dst[i], n8);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((bwd_dq16_kernel<D>), dim3(nqb * B * Hq), dim3(BWD_THREADS), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)rho,
-                       (const uint16_t*)d_o, lse, c_aux, G, dl, dq, drho, B, Hq, Hkv, T, scale,
+                       q16, k16, v16, r16, g16, lse, c_aux, G, dl, dq, drho, B, Hq, Hkv, T, scale,
                        scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv16_kernel<D>), dim3(nkb * B * Hkv), dim3(BWD_THREADS), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)rho,
-                       (const uint16_t*)d_o, lse, c_aux, G, dl, dk, dv, B, Hq, Hkv, T, scale,
+                       q16, k16, v16, r16, g16, lse, c_aux, G, dl, dk, dv, B, Hq, Hkv, T, scale,
                        scale * kLog2e);
     return hipGetLastError();
   } else {
@@ -824,6 +853,14 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
 }
 
 }  // namespace
+
+// Workspace of the backward: G and delta (fp32 per query row), then, for bf16
+// inputs, fp16 copies of q, rho, dO ([B, Hq, T, d]) and K, V ([B, Hkv, T, d]).
+size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int d) {
+  const size_t rows = (size_t)B * Hq * T;
+  return bwd_ws_align(2 * rows * sizeof(float)) +
+         (3 * rows * d + 2 * (size_t)B * Hkv * T * d) * sizeof(uint16_t);
+}
 
 hipError_t launch_bwd(int dtype, const void* q, const void* k, const void* v, const void* rho,
                       const void* d_o, const float* o, const float* lse, const float* c_aux,

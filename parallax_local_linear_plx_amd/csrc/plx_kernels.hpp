@@ -25,6 +25,8 @@ hipError_t launch_decode(int dtype, const void* q, const void* rho, const void* 
                          int Hq, int Hkv, int S_max, int d, float scale, int num_splits,
                          float* partials, hipStream_t stream);
 
+// Backward: workspace bytes (G and delta, then the fp16 input copies of the bf16 path).
+size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int d);
 hipError_t launch_bwd(int dtype, const void* q, const void* k, const void* v, const void* rho,
                       const void* d_o, const float* o, const float* lse, const float* c_aux,
                       const float* vbar_aux, float* dq, float* dk, float* dv, float* drho, int B,

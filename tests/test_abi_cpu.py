@@ -125,5 +125,12 @@ def test_bwd_validation(kw, status):
 
 
 def test_bwd_workspace_size():
-    assert binding.bwd_workspace_size(8, 16, 8, 4096, 128) == 2 * 8 * 16 * 4096 * 4
+    # G and delta (fp32 per query row, padded to 256 bytes), then fp16 copies of
+    # q, rho, dO ([B, Hq, T, d]) and k, v ([B, Hkv, T, d])
+    B, Hq, Hkv, T, d = 8, 16, 8, 4096, 128
+    head = (2 * B * Hq * T * 4 + 255) // 256 * 256
+    assert binding.bwd_workspace_size(B, Hq, Hkv, T, d) == head + (3 * B * Hq * T * d + 2 * B * Hkv * T * d) * 2
+    B, Hq, Hkv, T, d = 1, 2, 1, 3, 64
+    head = (2 * B * Hq * T * 4 + 255) // 256 * 256
+    assert binding.bwd_workspace_size(B, Hq, Hkv, T, d) == head + (3 * B * Hq * T * d + 2 * B * Hkv * T * d) * 2
     assert binding.bwd_workspace_size(8, 16, 8, 0, 128) == 0
