@@ -19,6 +19,7 @@
 //           query tiles of every head that shares the KV head, accumulates
 //           dV^T = dO^T Ptilde and dK^T = Q^T (tau dS) + rho^T dR.
 #include <algorithm>
+#include <type_traits>
 
 #include "plx_common.hpp"
 #include "plx_kernels.hpp"
@@ -542,10 +543,9 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq16_kernel(
     const int key0 = j * DQ_BC;
     const int buf = j & 1;
     if (j + 1 < ntiles) gload(key0 + DQ_BC);
-    if (key0 <= qw + 31) {
-      // rows past T hold zero operands and are never stored, so only the
-      // causal edge needs a mask
-      const bool diag = key0 + DQ_BC - 1 > qw;
+    // rows past T hold zero operands and are never stored, so only the causal
+    // edge needs a mask; tiles off the edge take a path without it
+    auto tile = [&](auto masked) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         f32x16 sa = zero16(), ra = zero16(), aa = zero16();
@@ -567,7 +567,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq16_kernel(
           for (int e = 0; e < 8; ++e) {
             const int a = 8 * s + e;
             float p = fast_exp2(__builtin_fmaf(sa[a], scale_log2, -lse2));
-            if (diag && key0 + 32 * st + acc_row(a, half) > my_q) p = 0.f;
+            if constexpr (decltype(masked)::value)
+              if (key0 + 32 * st + acc_row(a, half) > my_q) p = 0.f;
             const float r = ra[a], A = aa[a];
             const float t = di - A;
             dsop[e] = (_Float16)(p * __builtin_fmaf(A, k1, __builtin_fmaf(r, t, -k2)));
@@ -581,6 +582,11 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq16_kernel(
           }
         }
       }
+    };
+    if (key0 + DQ_BC - 1 > qw) {
+      if (key0 <= qw + 31) tile(std::true_type{});
+    } else {
+      tile(std::false_type{});
     }
     if (j + 1 < ntiles) lds_put((j + 1) & 1);  // buffer last read in iteration j-1
     __syncthreads();
@@ -738,21 +744,33 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv16_kernel(
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         f16x8 pop, dsop, drop;
+        float pv[8];
 #pragma unroll
         for (int i4 = 0; i4 < 2; ++i4) {
           const int r0 = 32 * st + 8 * (2 * s + i4) + 4 * half;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sc_[buf][0][r0]);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            pv[4 * i4 + jj] = fast_exp2(__builtin_fmaf(sa[8 * s + 4 * i4 + jj], scale_log2, -l4[jj]));
+        }
+        if (edge) {
+          asm volatile("");  // a real branch: most sub-tiles skip the mask
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int qi = qt0 + 32 * st + 8 * (2 * s + (e >> 2)) + 4 * half + (e & 3);
+            if (qi < my_k || qi >= T) pv[e] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int i4 = 0; i4 < 2; ++i4) {
+          const int r0 = 32 * st + 8 * (2 * s + i4) + 4 * half;
           const f32x4 k14 = *reinterpret_cast<const f32x4*>(&sc_[buf][1][r0]);
           const f32x4 k24 = *reinterpret_cast<const f32x4*>(&sc_[buf][2][r0]);
           const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sc_[buf][3][r0]);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int a = 8 * s + 4 * i4 + jj, e = 4 * i4 + jj;
-            float p = fast_exp2(__builtin_fmaf(sa[a], scale_log2, -l4[jj]));
-            if (edge) {
-              const int qi = qt0 + r0 + jj;
-              if (qi < my_k || qi >= T) p = 0.f;
-            }
+            const float p = pv[e];
             const float r = ra[a], A = aa[a];
             const float t = d4[jj] - A;
             pop[e] = (_Float16)(p * (k14[jj] - r));
