@@ -612,6 +612,210 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq16_kernel(
   }
 }
 
+// dQ and drho on 16x16x32 MFMA tiles, two waves per SIMD (bf16 inputs, read
+// from their fp16 copies).  The layout follows the forward kernel: a wave owns
+// 16 query rows (lane column c = lane % 16; the four 16-lane groups g split the
+// keys of a score tile and the head dimension of the gradient tiles).  Per
+// 32-key sub-tile:
+//   S^T, R^T = K [Q; rho]^T and A^T = V dO^T (32 keys x 16 queries), A = K / V
+//     rows from LDS, B = Q / rho / dO from registers;
+//   dS^T, dR^T in registers, rounded to the fp16 B operand of
+//   [dQ | drho]^T += K^T [dS | dR]^T, A = K^T from transpose reads of the K tile.
+// Workgroup: 8 waves, 128 query rows of one (b, h); 128-key K / V tiles
+// double-buffered in LDS, one barrier per tile.
+constexpr int DQB_BC = 128;
+template <int D>
+struct DqbSmem {
+  static constexpr int LD = D + 16;  // as the forward's tiles: conflict-free rows and transpose reads
+  alignas(16) _Float16 k[2][DQB_BC * LD];
+  alignas(16) _Float16 v[2][DQB_BC * LD];
+};
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_dq16b_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ rho, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
+    const float* __restrict__ c_aux, const float* __restrict__ Gv, const float* __restrict__ dlt,
+    float* __restrict__ dq, float* __restrict__ drho, int B, int Hq, int Hkv, int T, float scale,
+    float scale_log2) {
+  constexpr int NW = 8, NT = 64 * NW, BR = 16 * NW;
+  constexpr int NS = D / 32, ND = D / 16, CPR = D / 8;
+  constexpr int NCH = DQB_BC * CPR / NT;  // 16-byte chunks per thread per tile and tensor
+  using SM = DqbSmem<D>;
+  __shared__ SM sm;
+
+  const int nqb = (T + BR - 1) / BR;
+  const int bh_count = B * Hq;
+  const int lin = xcd_block_order(blockIdx.x, bh_count, nqb * bh_count);
+  const int qb = nqb - 1 - lin / bh_count;
+  const int bh = lin % bh_count;
+  const int b = bh / Hq, h = bh % Hq;
+  const int hk = h / (Hq / Hkv);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int q0 = qb * BR;
+  const int qw = q0 + 16 * wave;
+  const int my_q = qw + c;
+  const bool qvalid = my_q < T;
+
+  const size_t rowbase = (size_t)bh * T;
+  const uint16_t* kp = k + ((size_t)(b * Hkv + hk) * T) * D;
+  const uint16_t* vp = v + ((size_t)(b * Hkv + hk) * T) * D;
+  const int kend = min(T, q0 + BR);
+  const int ntiles = (kend + DQB_BC - 1) / DQB_BC;
+  const int nsub = (min(kend, qw + 16) + 31) / 32;
+
+  // global -> register staging of one tile (rows past T read row T-1: finite,
+  // and masked by the causal test since they follow every query)
+  u32x4 pk[NCH], pv[NCH];
+  auto gload = [&](int key0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int it = threadIdx.x + NT * i;
+      const size_t off = (size_t)min(key0 + it / CPR, T - 1) * D + (it % CPR) * 8;
+      pk[i] = *reinterpret_cast<const u32x4*>(kp + off);
+      pv[i] = *reinterpret_cast<const u32x4*>(vp + off);
+    }
+  };
+  auto lds_put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int it = threadIdx.x + NT * i;
+      const int o = (it / CPR) * SM::LD + (it % CPR) * 8;
+      *reinterpret_cast<u32x4*>(&sm.k[buf][o]) = pk[i];
+      *reinterpret_cast<u32x4*>(&sm.v[buf][o]) = pv[i];
+    }
+  };
+
+  gload(0);
+  f16x8 qop[NS], rop[NS], gop[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    u32x4 qa = {0u, 0u, 0u, 0u}, ra = qa, ga = qa;
+    if (qvalid) {
+      const size_t off = (rowbase + my_q) * D + 32 * s + 8 * g;
+      qa = *reinterpret_cast<const u32x4*>(q + off);
+      ra = *reinterpret_cast<const u32x4*>(rho + off);
+      ga = *reinterpret_cast<const u32x4*>(d_o + off);
+    }
+    qop[s] = __builtin_bit_cast(f16x8, qa);
+    rop[s] = __builtin_bit_cast(f16x8, ra);
+    gop[s] = __builtin_bit_cast(f16x8, ga);
+  }
+  const float lse2 = qvalid ? lse[rowbase + my_q] * kLog2e : 0.f;
+  const float ci = qvalid ? c_aux[rowbase + my_q] : 0.f;
+  const float Gi = qvalid ? Gv[rowbase + my_q] : 0.f;
+  const float di = qvalid ? dlt[rowbase + my_q] : 0.f;
+  // dS = p [A k1 + r (delta - A) - k2] with k1 = 1 + c, k2 = G + delta c
+  const float k1 = 1.f + ci, k2 = Gi + di * ci;
+  lds_put(0);
+  __syncthreads();
+
+  f32x4 dqa[ND], dra[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    dqa[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    dra[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto subtile = [&](int buf, int st, int kbase, auto masked) {
+    // scores S^T, R^T and A^T = V dO^T for 32 keys
+    unsigned kaddr = lds_addr(&sm.k[buf][(32 * st + c) * SM::LD + 8 * g]);
+    unsigned vaddr = lds_addr(&sm.v[buf][(32 * st + c) * SM::LD + 8 * g]);
+    asm volatile("" : "+v"(kaddr), "+v"(vaddr));
+    f16x8 ka[2][NS], va[2][NS];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        ka[t][s] = __builtin_bit_cast(f16x8, ld128_at(kaddr + 2 * (16 * t * SM::LD + 32 * s)));
+        va[t][s] = __builtin_bit_cast(f16x8, ld128_at(vaddr + 2 * (16 * t * SM::LD + 32 * s)));
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    f32x4 sacc[2], racc[2], aacc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[t][s], qop[s], s == 0 ? z : sacc[t], 0, 0, 0);
+        racc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[t][s], rop[s], s == 0 ? z : racc[t], 0, 0, 0);
+        aacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t][s], gop[s], s == 0 ? z : aacc[t], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // K^T operands of the gradient MFMAs, in flight during the elementwise part
+    unsigned taddr = lds_addr(&sm.k[buf][(32 * st + 4 * g + (c >> 2)) * SM::LD + 4 * (c & 3)]);
+    asm volatile("" : "+v"(taddr));
+    f16x8 kt[ND];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+      kt[dt] = __builtin_shufflevector(tr16_at(taddr + 2 * 16 * dt),
+                                       tr16_at(taddr + 2 * (16 * dt + 16 * SM::LD)), 0, 1, 2, 3, 4, 5, 6, 7);
+    __builtin_amdgcn_sched_barrier(0);
+    // dS^T, dR^T: element e of group g is key 16 (e / 4) + 4 g + e % 4, query c
+    f16x8 dsop, drop;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int t = e >> 2, j = e & 3;
+      float p = fast_exp2(__builtin_fmaf(sacc[t][j], scale_log2, -lse2));
+      if constexpr (decltype(masked)::value)
+        if (kbase + 16 * t + 4 * g + j > my_q) p = 0.f;
+      const float r = racc[t][j], A = aacc[t][j];
+      const float tt = di - A;
+      dsop[e] = (_Float16)(p * __builtin_fmaf(A, k1, __builtin_fmaf(r, tt, -k2)));
+      drop[e] = (_Float16)(p * tt);
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      dqa[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kt[dt], dsop, dqa[dt], 0, 0, 0);
+      dra[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kt[dt], drop, dra[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  auto iter = [&](int j, int buf) {
+    const int key0 = j * DQB_BC;
+    if (j + 1 < ntiles) gload(key0 + DQB_BC);
+#pragma unroll
+    for (int st = 0; st < DQB_BC / 32; ++st) {
+      const int kbase = key0 + 32 * st;
+      if (4 * j + st < nsub) {
+        if (kbase + 31 > qw)
+          subtile(buf, st, kbase, std::true_type{});
+        else
+          subtile(buf, st, kbase, std::false_type{});
+      }
+    }
+    if (j + 1 < ntiles) lds_put(buf ^ 1);
+    __syncthreads();
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    iter(j, 0);
+    if (j + 1 < ntiles) iter(j + 1, 1);
+  }
+
+  // dqa[dt][jj] is d = 16 dt + 4 g + jj of query c
+  if (qvalid) {
+    float* dqr = dq + (rowbase + my_q) * D;
+    float* drr = drho + (rowbase + my_q) * D;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      f32x4 x, y;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        x[jj] = scale * dqa[dt][jj];
+        y[jj] = dra[dt][jj];
+      }
+      *reinterpret_cast<f32x4*>(dqr + 16 * dt + 4 * g) = x;
+      *reinterpret_cast<f32x4*>(drr + 16 * dt + 4 * g) = y;
+    }
+  }
+}
+
 // dK and dV, key-outer (bf16 inputs, read from their fp16 copies): the query
 // tiles of all G heads of the KV head form one sequence, prefetched one tile
 // ahead.
@@ -846,7 +1050,8 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
                          (f16x8*)dst[i], n8);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_dq16_kernel<D>), dim3(nqb * B * Hq), dim3(BWD_THREADS), 0, stream,
+    const int nqb16 = (T + 127) / 128;
+    hipLaunchKernelGGL((bwd_dq16b_kernel<D>), dim3(nqb16 * B * Hq), dim3(512), 0, stream,
                        q16, k16, v16, r16, g16, lse, c_aux, G, dl, dq, drho, B, Hq, Hkv, T, scale,
                        scale * kLog2e);
     e = hipGetLastError();

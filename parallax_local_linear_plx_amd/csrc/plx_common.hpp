@@ -204,4 +204,19 @@ __device__ __forceinline__ typename Pol::vop_t load_t_op(const typename Pol::vel
   return a;
 }
 
+// LDS byte address of a shared-memory pointer, and transpose / 16-byte reads
+// at such an address.  A base address the compiler cannot see through keeps
+// every per-read displacement in the instruction's offset field.
+typedef short lds_s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(size_t)((__attribute__((address_space(3))) const char*)p);
+}
+__device__ __forceinline__ f16x4 tr16_at(unsigned a) {
+  lds_s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) lds_s16x4*)(size_t)a);
+  return __builtin_bit_cast(f16x4, t);
+}
+__device__ __forceinline__ u32x4 ld128_at(unsigned a) {
+  return *(__attribute__((address_space(3))) const u32x4*)(size_t)a;
+}
+
 }  // namespace plx

@@ -484,24 +484,6 @@ struct Fwd16Smem {
   alignas(16) _Float16 v[2][F16_BC * VLD];
 };
 
-__device__ __forceinline__ f16x4 tr16_f16(const _Float16* p) {
-  s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(f16x4, t);
-}
-
-// LDS byte address of a shared-memory pointer, and transpose / 16-byte reads
-// at such an address.  A base address the compiler cannot see through keeps
-// every per-read displacement in the instruction's offset field.
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return (unsigned)(size_t)((__attribute__((address_space(3))) const char*)p);
-}
-__device__ __forceinline__ f16x4 tr16_at(unsigned a) {
-  s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(size_t)a);
-  return __builtin_bit_cast(f16x4, t);
-}
-__device__ __forceinline__ u32x4 ld128_at(unsigned a) {
-  return *(__attribute__((address_space(3))) const u32x4*)(size_t)a;
-}
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
