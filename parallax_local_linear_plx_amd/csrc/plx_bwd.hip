@@ -1017,6 +1017,238 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv16_kernel(
   }
 }
 
+// dK and dV on 16x16x32 MFMA tiles, two waves per SIMD (bf16 inputs, read
+// from their fp16 copies).  A wave owns 16 keys (lane column c = lane % 16 is
+// the key; the 16-lane groups g split the queries of a score tile and the head
+// dimension of the gradient tiles).  Per 32-query sub-tile:
+//   S, R = [Q; rho] K^T and A = dO V^T (32 queries x 16 keys), A operand = Q /
+//     rho / dO rows from LDS, B = K / V from registers;
+//   P (1 + c - r), tau dS and dR in registers, rounded to the fp16 B operands of
+//   dV^T += dO^T [P (1 + c - r)],  dK^T += Q^T [tau dS] + rho^T dR,
+//   A = Q^T / rho^T / dO^T from transpose reads of the query tiles.
+// Workgroup: 8 waves, 128 keys of one KV head; the 64-row query tiles of all G
+// query heads form one sequence, double-buffered in LDS, one barrier per tile.
+constexpr int DKB_BQ = 64;
+template <int D>
+struct DkbSmem {
+  static constexpr int LD = D + 16;
+  alignas(16) _Float16 q[2][DKB_BQ * LD];
+  alignas(16) _Float16 r[2][DKB_BQ * LD];
+  alignas(16) _Float16 g[2][DKB_BQ * LD];
+  alignas(16) float sc[2][4][DKB_BQ];  // per query row: lse * log2e, 1 + c, G + delta c, delta
+};
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv16b_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ rho, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
+    const float* __restrict__ c_aux, const float* __restrict__ Gv, const float* __restrict__ dlt,
+    float* __restrict__ dk, float* __restrict__ dv, int B, int Hq, int Hkv, int T, float scale,
+    float scale_log2) {
+  constexpr int NW = 8, NT = 64 * NW, BK = 16 * NW;
+  constexpr int NS = D / 32, ND = D / 16, CPR = D / 8;
+  constexpr int NCH = DKB_BQ * CPR / NT;  // 16-byte chunks per thread per tile and tensor
+  using SM = DkbSmem<D>;
+  __shared__ SM sm;
+
+  const int bhk_count = B * Hkv;
+  const int kb = blockIdx.x / bhk_count;
+  const int bhk = blockIdx.x % bhk_count;
+  const int b = bhk / Hkv, hk = bhk % Hkv;
+  const int G = Hq / Hkv;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int k0 = kb * BK;
+  const int kw = k0 + 16 * wave;
+  const int my_k = kw + c;
+  const bool kvalid = my_k < T;
+
+  const size_t kvbase = (size_t)bhk * T;
+  const int nqt = (T - k0 + DKB_BQ - 1) / DKB_BQ;  // query tiles per head (queries >= k0)
+  const int ntile = G * nqt;
+
+  u32x4 pq[NCH], pr[NCH], pg[NCH];
+  float psc[4];
+  auto tile_rows = [&](int n, size_t& rowbase, int& qt0) {
+    const int hh = n / nqt;
+    qt0 = k0 + (n - hh * nqt) * DKB_BQ;
+    rowbase = ((size_t)b * Hq + hk * G + hh) * T;
+  };
+  auto gload = [&](int n) {
+    size_t rowbase;
+    int qt0;
+    tile_rows(n, rowbase, qt0);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int it = threadIdx.x + NT * i;
+      const size_t off = (rowbase + min(qt0 + it / CPR, T - 1)) * D + (it % CPR) * 8;
+      pq[i] = *reinterpret_cast<const u32x4*>(q + off);
+      pr[i] = *reinterpret_cast<const u32x4*>(rho + off);
+      pg[i] = *reinterpret_cast<const u32x4*>(d_o + off);
+    }
+    if (threadIdx.x < DKB_BQ) {
+      const size_t r = rowbase + min(qt0 + (int)threadIdx.x, T - 1);
+      psc[0] = lse[r];
+      psc[1] = c_aux[r];
+      psc[2] = Gv[r];
+      psc[3] = dlt[r];
+    }
+  };
+  auto lds_put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int it = threadIdx.x + NT * i;
+      const int o = (it / CPR) * SM::LD + (it % CPR) * 8;
+      *reinterpret_cast<u32x4*>(&sm.q[buf][o]) = pq[i];
+      *reinterpret_cast<u32x4*>(&sm.r[buf][o]) = pr[i];
+      *reinterpret_cast<u32x4*>(&sm.g[buf][o]) = pg[i];
+    }
+    if (threadIdx.x < DKB_BQ) {
+      sm.sc[buf][0][threadIdx.x] = psc[0] * kLog2e;
+      sm.sc[buf][1][threadIdx.x] = 1.f + psc[1];
+      sm.sc[buf][2][threadIdx.x] = psc[2] + psc[3] * psc[1];
+      sm.sc[buf][3][threadIdx.x] = psc[3];
+    }
+  };
+
+  gload(0);
+  f16x8 kop[NS], vop[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    u32x4 ka = {0u, 0u, 0u, 0u}, va = ka;
+    if (kvalid) {
+      const size_t off = (kvbase + my_k) * D + 32 * s + 8 * g;
+      ka = *reinterpret_cast<const u32x4*>(k + off);
+      va = *reinterpret_cast<const u32x4*>(v + off);
+    }
+    kop[s] = __builtin_bit_cast(f16x8, ka);
+    vop[s] = __builtin_bit_cast(f16x8, va);
+  }
+  lds_put(0);
+  __syncthreads();
+
+  f32x4 dka[ND], dva[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    dka[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    dva[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+
+  // one 32-query sub-tile st of the tile in buffer buf (first query qs)
+  auto subtile = [&](int buf, int st, int qs, auto masked) {
+    f32x4 sacc[2], racc[2], aacc[2];
+    {
+      unsigned qa = lds_addr(&sm.q[buf][(32 * st + c) * SM::LD + 8 * g]);
+      unsigned ra = lds_addr(&sm.r[buf][(32 * st + c) * SM::LD + 8 * g]);
+      unsigned ga = lds_addr(&sm.g[buf][(32 * st + c) * SM::LD + 8 * g]);
+      asm volatile("" : "+v"(qa), "+v"(ra), "+v"(ga));
+      // one 16-query tile at a time: its twelve operands are read before its MFMAs
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f16x8 qo[NS], ro[NS], go[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const unsigned off = 2 * (16 * t * SM::LD + 32 * s);
+          qo[s] = __builtin_bit_cast(f16x8, ld128_at(qa + off));
+          ro[s] = __builtin_bit_cast(f16x8, ld128_at(ra + off));
+          go[s] = __builtin_bit_cast(f16x8, ld128_at(ga + off));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qo[s], kop[s], s == 0 ? z : sacc[t], 0, 0, 0);
+          racc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ro[s], kop[s], s == 0 ? z : racc[t], 0, 0, 0);
+          aacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(go[s], vop[s], s == 0 ? z : aacc[t], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+    // accumulator element j of key tile t: query qs + 16 t + 4 g + j, key c;
+    // the same order as the K index of the transpose-read A operands below
+    f16x8 pop, dsop, drop;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int r0 = 32 * st + 16 * t + 4 * g;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.sc[buf][0][r0]);
+      const f32x4 k14 = *reinterpret_cast<const f32x4*>(&sm.sc[buf][1][r0]);
+      const f32x4 k24 = *reinterpret_cast<const f32x4*>(&sm.sc[buf][2][r0]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.sc[buf][3][r0]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float p = fast_exp2(__builtin_fmaf(sacc[t][j], scale_log2, -l4[j]));
+        if constexpr (decltype(masked)::value) {
+          const int qi = qs + 16 * t + 4 * g + j;
+          if (qi < my_k || qi >= T) p = 0.f;
+        }
+        const float r = racc[t][j], A = aacc[t][j];
+        const float tt = d4[j] - A;
+        pop[4 * t + j] = (_Float16)(p * (k14[j] - r));
+        dsop[4 * t + j] = (_Float16)((scale * p) * __builtin_fmaf(A, k14[j], __builtin_fmaf(r, tt, -k24[j])));
+        drop[4 * t + j] = (_Float16)(p * tt);
+      }
+    }
+    // gradient MFMAs: A = Q^T / rho^T / dO^T, 16 d rows x 32 queries each
+    unsigned tq = lds_addr(&sm.q[buf][(32 * st + 4 * g + (c >> 2)) * SM::LD + 4 * (c & 3)]);
+    unsigned tr = lds_addr(&sm.r[buf][(32 * st + 4 * g + (c >> 2)) * SM::LD + 4 * (c & 3)]);
+    unsigned tg = lds_addr(&sm.g[buf][(32 * st + 4 * g + (c >> 2)) * SM::LD + 4 * (c & 3)]);
+    asm volatile("" : "+v"(tq), "+v"(tr), "+v"(tg));
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      const unsigned o0 = 2 * 16 * dt, o1 = 2 * (16 * dt + 16 * SM::LD);
+      const f16x8 aq = __builtin_shufflevector(tr16_at(tq + o0), tr16_at(tq + o1), 0, 1, 2, 3, 4, 5, 6, 7);
+      const f16x8 ar = __builtin_shufflevector(tr16_at(tr + o0), tr16_at(tr + o1), 0, 1, 2, 3, 4, 5, 6, 7);
+      const f16x8 ag = __builtin_shufflevector(tr16_at(tg + o0), tr16_at(tg + o1), 0, 1, 2, 3, 4, 5, 6, 7);
+      dva[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ag, pop, dva[dt], 0, 0, 0);
+      dka[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, dsop, dka[dt], 0, 0, 0);
+      dka[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ar, drop, dka[dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  auto iter = [&](int n, int buf) {
+    size_t rowbase_unused;
+    int qt0;
+    tile_rows(n, rowbase_unused, qt0);
+    if (n + 1 < ntile) gload(n + 1);
+#pragma unroll
+    for (int st = 0; st < DKB_BQ / 32; ++st) {
+      const int qs = qt0 + 32 * st;
+      if (qs + 31 < kw) continue;  // every query of the sub-tile precedes every key of the wave
+      if (qs < kw + 15 || qs + 31 >= T)
+        subtile(buf, st, qs, std::true_type{});
+      else
+        subtile(buf, st, qs, std::false_type{});
+    }
+    if (n + 1 < ntile) lds_put(buf ^ 1);  // buffer last read in iteration n-1
+    __syncthreads();
+  };
+  for (int n = 0; n < ntile; n += 2) {
+    iter(n, 0);
+    if (n + 1 < ntile) iter(n + 1, 1);
+  }
+
+  // dka[dt][jj] is d = 16 dt + 4 g + jj of key c
+  if (kvalid) {
+    float* dkr = dk + (kvbase + my_k) * D;
+    float* dvr = dv + (kvbase + my_k) * D;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      f32x4 x, y;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        x[jj] = dka[dt][jj];
+        y[jj] = dva[dt][jj];
+      }
+      *reinterpret_cast<f32x4*>(dkr + 16 * dt + 4 * g) = x;
+      *reinterpret_cast<f32x4*>(dvr + 16 * dt + 4 * g) = y;
+    }
+  }
+}
+
 template <class Pol, int D>
 hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* rho,
                         const void* d_o, const float* o, const float* lse, const float* c_aux,
@@ -1056,7 +1288,7 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
                        scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv16_kernel<D>), dim3(nkb * B * Hkv), dim3(BWD_THREADS), 0, stream,
+    hipLaunchKernelGGL((bwd_dkdv16b_kernel<D>), dim3(nkb * B * Hkv), dim3(512), 0, stream,
                        q16, k16, v16, r16, g16, lse, c_aux, G, dl, dk, dv, B, Hq, Hkv, T, scale,
                        scale * kLog2e);
     return hipGetLastError();
