@@ -10,14 +10,18 @@
 //   dR_ij = -w_ij (A_ij - delta_i)
 //   dQ = tau dS K,  dK = tau dS^T Q + dR^T rho,  drho = dR K.
 //
-// Three kernels, no atomics (the result is deterministic):
+// Kernels, no atomics (the result is deterministic):
 //   pre   : G and delta per row.
+//   cvt   : (bf16 inputs) fp16 copies of q, rho, dO, k and v in the workspace.
 //   dq    : query-outer, laid out like the forward (S^T = K Q^T, one query per
 //           lane column): recomputes S, R and A^T = V dO^T per key tile, forms
 //           dS, dR in registers and accumulates dQ^T = K^T dS^T, drho^T = K^T dR^T.
 //   dkdv  : key-outer: one key per lane column (S = Q K^T), loops over the
 //           query tiles of every head that shares the KV head, accumulates
 //           dV^T = dO^T Ptilde and dK^T = Q^T (tau dS) + rho^T dR.
+// The bf16 dq and dkdv kernels run 16-row waves on 16x16x32 fp16 MFMAs, two
+// waves per SIMD; the fp32 ones (the exact-parity path) 32-row waves on fp32
+// MFMAs.
 #include <algorithm>
 #include <type_traits>
 
@@ -395,40 +399,12 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// bf16 path.  Q, rho, dO, K and V enter both kernels' MFMAs as fp16: the
-// bf16 -> fp16 conversion is exact over fp16's normal range, and fp16
-// operands let one row-major LDS tile serve both the score GEMMs (rows read
-// with ds_read_b128) and the transposed value GEMMs (ds_read_b64_tr_b16).
-// Tiles are double-buffered: the next tile's global loads are issued at the
-// top of an iteration, converted and stored at its end (into the buffer read
-// one iteration earlier), followed by the iteration's single barrier.
-// Rows past T are loaded as row T-1 (finite) and given p = 0.
+// bf16 path.  Q, rho, dO, K and V enter every MFMA of the two main kernels as
+// fp16: the bf16 -> fp16 conversion is exact over fp16's normal range, and
+// fp16 operands let one row-major LDS tile serve both the score GEMMs (rows
+// read with ds_read_b128) and the gradient GEMMs (transpose reads,
+// ds_read_b64_tr_b16).  A conversion pass writes the fp16 copies once.
 inline size_t bwd_ws_align(size_t n) { return (n + 255) & ~(size_t)255; }
-constexpr int B16_LD = 24;  // row padding (halves): ds_read_b128 rows and transpose reads spread over the banks
-
-__device__ __forceinline__ f16x4 tr_read(const _Float16* p) {
-  typedef short s16x4_t __attribute__((ext_vector_type(4)));
-  s16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(p));
-  return __builtin_bit_cast(f16x4, t);
-}
-
-// Value-GEMM A operand from a row-major fp16 tile: element e of lane
-// (column col0 + lane % 32, half h) is tile[row0 + acc_row(8 s + e, h)][col0 + lane % 32],
-// matching a B operand taken from slots 8 s .. 8 s + 7 of a 32x32 accumulator.
-// ds_read_b64_tr_b16 hands lane i of each 16-lane block element i % 4 of the
-// chunks addressed by lanes 4 e + i / 4 of that block.
-__device__ __forceinline__ f16x8 tr_op(const _Float16* tile, int ld, int row0, int col0, int s, int lane) {
-  const int h = lane >> 5, blk = (lane >> 4) & 1, li = lane & 15;
-  const _Float16* base = tile + (row0 + 16 * s + 4 * h + (li >> 2)) * ld + col0 + 16 * blk + 4 * (li & 3);
-  const f16x4 lo = tr_read(base), hi = tr_read(base + 8 * ld);
-  f16x8 a;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    a[e] = lo[e];
-    a[4 + e] = hi[e];
-  }
-  return a;
-}
 
 __device__ __forceinline__ f16x8 cvt_bf16x8_f16(u32x4 raw) {
   const u16x8 b = __builtin_bit_cast(u16x8, raw);
@@ -445,171 +421,6 @@ __global__ __launch_bounds__(256) void cvt_f16_kernel(const u32x4* __restrict__ 
                                                      long long n8) {
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long long)gridDim.x * 256)
     dst[i] = cvt_bf16x8_f16(src[i]);
-}
-
-__device__ __forceinline__ f32x16 mma16(f16x8 a, f16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-// dQ and drho, query-outer (bf16 inputs; q, k, v, rho and dO point to their
-// fp16 copies).
-template <int D>
-__global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dq16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ rho, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
-    const float* __restrict__ c_aux, const float* __restrict__ Gv, const float* __restrict__ dlt,
-    float* __restrict__ dq, float* __restrict__ drho, int B, int Hq, int Hkv, int T, float scale,
-    float scale_log2) {
-  constexpr int NS = D / 16, ND = D / 32;
-  constexpr int LD = D + B16_LD;
-  constexpr int CPR = D / 8;
-  constexpr int NCH = DQ_BC * CPR / BWD_THREADS;  // 16-byte chunks per thread per tile and tensor
-  __shared__ alignas(16) _Float16 ks[2][DQ_BC * LD];
-  __shared__ alignas(16) _Float16 vs[2][DQ_BC * LD];
-
-  const int nqb = (T + DQ_BR - 1) / DQ_BR;
-  const int bh_count = B * Hq;
-  const int lin = xcd_block_order(blockIdx.x, bh_count, nqb * bh_count);
-  const int qb = nqb - 1 - lin / bh_count;
-  const int bh = lin % bh_count;
-  const int b = bh / Hq, h = bh % Hq;
-  const int hk = h / (Hq / Hkv);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 31, half = lane >> 5;
-  const int q0 = qb * DQ_BR;
-  const int qw = q0 + 32 * wave;
-  const int my_q = qw + col;
-  const bool qvalid = my_q < T;
-
-  const size_t rowbase = (size_t)bh * T;
-  const uint16_t* kp = k + ((size_t)(b * Hkv + hk) * T) * D;
-  const uint16_t* vp = v + ((size_t)(b * Hkv + hk) * T) * D;
-  const int kend = min(T, q0 + DQ_BR);
-  const int ntiles = (kend + DQ_BC - 1) / DQ_BC;
-
-  u32x4 pk[NCH], pv[NCH];
-  auto gload = [&](int key0) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int it = threadIdx.x + BWD_THREADS * i;
-      const size_t off = (size_t)min(key0 + it / CPR, T - 1) * D + (it % CPR) * 8;
-      pk[i] = *reinterpret_cast<const u32x4*>(kp + off);
-      pv[i] = *reinterpret_cast<const u32x4*>(vp + off);
-    }
-  };
-  auto lds_put = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int it = threadIdx.x + BWD_THREADS * i;
-      const int o = (it / CPR) * LD + (it % CPR) * 8;
-      *reinterpret_cast<f16x8*>(&ks[buf][o]) = __builtin_bit_cast(f16x8, pk[i]);
-      *reinterpret_cast<f16x8*>(&vs[buf][o]) = __builtin_bit_cast(f16x8, pv[i]);
-    }
-  };
-
-  gload(0);
-  f16x8 qop[NS], rop[NS], gop[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4 qa = {0u, 0u, 0u, 0u}, ra = qa, ga = qa;
-    if (qvalid) {
-      const size_t off = (rowbase + my_q) * D + 16 * s + 8 * half;
-      qa = *reinterpret_cast<const u32x4*>(q + off);
-      ra = *reinterpret_cast<const u32x4*>(rho + off);
-      ga = *reinterpret_cast<const u32x4*>(d_o + off);
-    }
-    qop[s] = __builtin_bit_cast(f16x8, qa);
-    rop[s] = __builtin_bit_cast(f16x8, ra);
-    gop[s] = __builtin_bit_cast(f16x8, ga);
-  }
-  const float lse2 = qvalid ? lse[rowbase + my_q] * kLog2e : 0.f;
-  const float ci = qvalid ? c_aux[rowbase + my_q] : 0.f;
-  const float Gi = qvalid ? Gv[rowbase + my_q] : 0.f;
-  const float di = qvalid ? dlt[rowbase + my_q] : 0.f;
-  // dS = p [(1 + c - r) A - G + delta (r - c)] = p [A k1 + r (delta - A) - k2]
-  const float k1 = 1.f + ci, k2 = Gi + di * ci;
-  lds_put(0);
-  __syncthreads();
-
-  f32x16 dqa[ND], dra[ND];
-#pragma unroll
-  for (int i = 0; i < ND; ++i) {
-    dqa[i] = zero16();
-    dra[i] = zero16();
-  }
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int key0 = j * DQ_BC;
-    const int buf = j & 1;
-    if (j + 1 < ntiles) gload(key0 + DQ_BC);
-    // rows past T hold zero operands and are never stored, so only the causal
-    // edge needs a mask; tiles off the edge take a path without it
-    auto tile = [&](auto masked) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        f32x16 sa = zero16(), ra = zero16(), aa = zero16();
-        const _Float16* krow = &ks[buf][(32 * st + col) * LD + 8 * half];
-        const _Float16* vrow = &vs[buf][(32 * st + col) * LD + 8 * half];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const f16x8 ak = *reinterpret_cast<const f16x8*>(krow + 16 * s);
-          const f16x8 av = *reinterpret_cast<const f16x8*>(vrow + 16 * s);
-          sa = mma16(ak, qop[s], sa);
-          ra = mma16(ak, rop[s], ra);
-          aa = mma16(av, gop[s], aa);
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          // dS^T and dR^T of 8 keys, straight into the fp16 operands
-          f16x8 dsop, drop;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int a = 8 * s + e;
-            float p = fast_exp2(__builtin_fmaf(sa[a], scale_log2, -lse2));
-            if constexpr (decltype(masked)::value)
-              if (key0 + 32 * st + acc_row(a, half) > my_q) p = 0.f;
-            const float r = ra[a], A = aa[a];
-            const float t = di - A;
-            dsop[e] = (_Float16)(p * __builtin_fmaf(A, k1, __builtin_fmaf(r, t, -k2)));
-            drop[e] = (_Float16)(p * t);
-          }
-#pragma unroll
-          for (int dt = 0; dt < ND; ++dt) {
-            const f16x8 a = tr_op(ks[buf], LD, 32 * st, 32 * dt, s, lane);
-            dqa[dt] = mma16(a, dsop, dqa[dt]);
-            dra[dt] = mma16(a, drop, dra[dt]);
-          }
-        }
-      }
-    };
-    if (key0 + DQ_BC - 1 > qw) {
-      if (key0 <= qw + 31) tile(std::true_type{});
-    } else {
-      tile(std::false_type{});
-    }
-    if (j + 1 < ntiles) lds_put((j + 1) & 1);  // buffer last read in iteration j-1
-    __syncthreads();
-  }
-
-  if (qvalid) {
-    float* dqr = dq + (rowbase + my_q) * D;
-    float* drr = drho + (rowbase + my_q) * D;
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = 32 * dt + 8 * i + 4 * half;
-        f32x4 x, y;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          x[jj] = scale * dqa[dt][4 * i + jj];
-          y[jj] = dra[dt][4 * i + jj];
-        }
-        *reinterpret_cast<f32x4*>(dqr + d0) = x;
-        *reinterpret_cast<f32x4*>(drr + d0) = y;
-      }
-  }
 }
 
 // dQ and drho on 16x16x32 MFMA tiles, two waves per SIMD (bf16 inputs, read
@@ -813,207 +624,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16b_kernel(
       *reinterpret_cast<f32x4*>(dqr + 16 * dt + 4 * g) = x;
       *reinterpret_cast<f32x4*>(drr + 16 * dt + 4 * g) = y;
     }
-  }
-}
-
-// dK and dV, key-outer (bf16 inputs, read from their fp16 copies): the query
-// tiles of all G heads of the KV head form one sequence, prefetched one tile
-// ahead.
-template <int D>
-__global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv16_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ rho, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
-    const float* __restrict__ c_aux, const float* __restrict__ Gv, const float* __restrict__ dlt,
-    float* __restrict__ dk, float* __restrict__ dv, int B, int Hq, int Hkv, int T, float scale,
-    float scale_log2) {
-  constexpr int BQ = 64;
-  constexpr int NS = D / 16, ND = D / 32;
-  constexpr int LD = D + B16_LD;
-  constexpr int CPR = D / 8;
-  constexpr int NCH = BQ * CPR / BWD_THREADS;
-  __shared__ alignas(16) _Float16 qs_[2][BQ * LD];
-  __shared__ alignas(16) _Float16 rs_[2][BQ * LD];
-  __shared__ alignas(16) _Float16 gs_[2][BQ * LD];
-  __shared__ alignas(16) float sc_[2][4][BQ];  // lse * log2e, 1 + c, G + delta c, delta
-
-  const int bhk_count = B * Hkv;
-  const int lin = blockIdx.x;
-  const int kb = lin / bhk_count;
-  const int bhk = lin % bhk_count;
-  const int b = bhk / Hkv, hk = bhk % Hkv;
-  const int G = Hq / Hkv;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 31, half = lane >> 5;
-  const int k0 = kb * KV_BK;
-  const int kw = k0 + 32 * wave;
-  const int my_k = kw + col;
-  const bool kvalid = my_k < T;
-
-  const size_t kvbase = (size_t)bhk * T;
-  const int nqt = (T - k0 + BQ - 1) / BQ;  // query tiles per head (queries >= k0)
-  const int ntile = G * nqt;
-
-  u32x4 pq[NCH], pr[NCH], pg[NCH];
-  float psc[4];
-  auto tile_rows = [&](int n, size_t& rowbase, int& qt0) {
-    const int hh = n / nqt;
-    qt0 = k0 + (n - hh * nqt) * BQ;
-    rowbase = ((size_t)b * Hq + hk * G + hh) * T;
-  };
-  auto gload = [&](int n) {
-    size_t rowbase;
-    int qt0;
-    tile_rows(n, rowbase, qt0);
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int it = threadIdx.x + BWD_THREADS * i;
-      const size_t off = (rowbase + min(qt0 + it / CPR, T - 1)) * D + (it % CPR) * 8;
-      pq[i] = *reinterpret_cast<const u32x4*>(q + off);
-      pr[i] = *reinterpret_cast<const u32x4*>(rho + off);
-      pg[i] = *reinterpret_cast<const u32x4*>(d_o + off);
-    }
-    if (threadIdx.x < BQ) {
-      const size_t r = rowbase + min(qt0 + (int)threadIdx.x, T - 1);
-      psc[0] = lse[r];
-      psc[1] = c_aux[r];
-      psc[2] = Gv[r];
-      psc[3] = dlt[r];
-    }
-  };
-  auto lds_put = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int it = threadIdx.x + BWD_THREADS * i;
-      const int o = (it / CPR) * LD + (it % CPR) * 8;
-      *reinterpret_cast<f16x8*>(&qs_[buf][o]) = __builtin_bit_cast(f16x8, pq[i]);
-      *reinterpret_cast<f16x8*>(&rs_[buf][o]) = __builtin_bit_cast(f16x8, pr[i]);
-      *reinterpret_cast<f16x8*>(&gs_[buf][o]) = __builtin_bit_cast(f16x8, pg[i]);
-    }
-    if (threadIdx.x < BQ) {
-      // per query row: lse * log2e, k1 = 1 + c, k2 = G + delta c, delta
-      sc_[buf][0][threadIdx.x] = psc[0] * kLog2e;
-      sc_[buf][1][threadIdx.x] = 1.f + psc[1];
-      sc_[buf][2][threadIdx.x] = psc[2] + psc[3] * psc[1];
-      sc_[buf][3][threadIdx.x] = psc[3];
-    }
-  };
-
-  gload(0);
-  f16x8 kop[NS], vop[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4 ka = {0u, 0u, 0u, 0u}, va = ka;
-    if (kvalid) {
-      const size_t off = (kvbase + my_k) * D + 16 * s + 8 * half;
-      ka = *reinterpret_cast<const u32x4*>(k + off);
-      va = *reinterpret_cast<const u32x4*>(v + off);
-    }
-    kop[s] = __builtin_bit_cast(f16x8, ka);
-    vop[s] = __builtin_bit_cast(f16x8, va);
-  }
-  lds_put(0);
-  __syncthreads();
-
-  f32x16 dka[ND], dva[ND];
-#pragma unroll
-  for (int i = 0; i < ND; ++i) {
-    dka[i] = zero16();
-    dva[i] = zero16();
-  }
-
-  for (int n = 0; n < ntile; ++n) {
-    const int buf = n & 1;
-    size_t rowbase_unused;
-    int qt0;
-    tile_rows(n, rowbase_unused, qt0);
-    if (n + 1 < ntile) gload(n + 1);
-#pragma unroll
-    for (int st = 0; st < BQ / 32; ++st) {
-      const int qs = qt0 + 32 * st;
-      if (qs + 31 < kw) continue;  // every query of the sub-tile precedes every key of the wave
-      f32x16 sa = zero16(), ra = zero16(), aa = zero16();
-      const _Float16* qrow = &qs_[buf][(32 * st + col) * LD + 8 * half];
-      const _Float16* rrow = &rs_[buf][(32 * st + col) * LD + 8 * half];
-      const _Float16* grow = &gs_[buf][(32 * st + col) * LD + 8 * half];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        sa = mma16(*reinterpret_cast<const f16x8*>(qrow + 16 * s), kop[s], sa);
-        ra = mma16(*reinterpret_cast<const f16x8*>(rrow + 16 * s), kop[s], ra);
-        aa = mma16(*reinterpret_cast<const f16x8*>(grow + 16 * s), vop[s], aa);
-      }
-      // lane column = key my_k; accumulator slot a = query qs + acc_row(a, half).
-      // Masked: queries before the key (the diagonal sub-tile) and rows past T.
-      const bool edge = qs < kw + 31 || qs + 31 >= T;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        f16x8 pop, dsop, drop;
-        float pv[8];
-#pragma unroll
-        for (int i4 = 0; i4 < 2; ++i4) {
-          const int r0 = 32 * st + 8 * (2 * s + i4) + 4 * half;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sc_[buf][0][r0]);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            pv[4 * i4 + jj] = fast_exp2(__builtin_fmaf(sa[8 * s + 4 * i4 + jj], scale_log2, -l4[jj]));
-        }
-        if (edge) {
-          asm volatile("");  // a real branch: most sub-tiles skip the mask
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int qi = qt0 + 32 * st + 8 * (2 * s + (e >> 2)) + 4 * half + (e & 3);
-            if (qi < my_k || qi >= T) pv[e] = 0.f;
-          }
-        }
-#pragma unroll
-        for (int i4 = 0; i4 < 2; ++i4) {
-          const int r0 = 32 * st + 8 * (2 * s + i4) + 4 * half;
-          const f32x4 k14 = *reinterpret_cast<const f32x4*>(&sc_[buf][1][r0]);
-          const f32x4 k24 = *reinterpret_cast<const f32x4*>(&sc_[buf][2][r0]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sc_[buf][3][r0]);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int a = 8 * s + 4 * i4 + jj, e = 4 * i4 + jj;
-            const float p = pv[e];
-            const float r = ra[a], A = aa[a];
-            const float t = d4[jj] - A;
-            pop[e] = (_Float16)(p * (k14[jj] - r));
-            dsop[e] = (_Float16)((scale * p) * __builtin_fmaf(A, k14[jj], __builtin_fmaf(r, t, -k24[jj])));
-            drop[e] = (_Float16)(p * t);
-          }
-        }
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
-          const f16x8 ag = tr_op(gs_[buf], LD, 32 * st, 32 * dt, s, lane);
-          const f16x8 aq = tr_op(qs_[buf], LD, 32 * st, 32 * dt, s, lane);
-          const f16x8 ar = tr_op(rs_[buf], LD, 32 * st, 32 * dt, s, lane);
-          dva[dt] = mma16(ag, pop, dva[dt]);
-          dka[dt] = mma16(aq, dsop, dka[dt]);
-          dka[dt] = mma16(ar, drop, dka[dt]);
-        }
-      }
-    }
-    if (n + 1 < ntile) lds_put((n + 1) & 1);  // buffer last read in iteration n-1
-    __syncthreads();
-  }
-
-  if (kvalid) {
-    float* dkr = dk + (kvbase + my_k) * D;
-    float* dvr = dv + (kvbase + my_k) * D;
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = 32 * dt + 8 * i + 4 * half;
-        f32x4 x, y;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          x[jj] = dka[dt][4 * i + jj];
-          y[jj] = dva[dt][4 * i + jj];
-        }
-        *reinterpret_cast<f32x4*>(dkr + d0) = x;
-        *reinterpret_cast<f32x4*>(dvr + d0) = y;
-      }
   }
 }
 
