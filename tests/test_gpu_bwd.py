@@ -46,7 +46,12 @@ def test_fp32_gradients(gpu_lib, B, Hq, Hkv, T, d):
         check_fp32(got[n], ref[n], n, floor=grad_floor(ref[n]))
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,T,d", [(1, 4, 2, 300, 128), (1, 2, 2, 129, 64), (2, 2, 1, 77, 128)])
+@pytest.mark.parametrize("B,Hq,Hkv,T,d", [
+    (1, 4, 2, 300, 128), (1, 2, 2, 129, 64), (2, 2, 1, 77, 128),
+    (1, 1, 1, 1, 128),     # a single row
+    (1, 8, 2, 513, 64),    # G = 4; several 128-key blocks and 64-row query tiles, ragged tail
+    (1, 16, 1, 200, 128),  # G = 16: one KV head shared by sixteen query heads
+])
 def test_bf16_gradients(gpu_lib, B, Hq, Hkv, T, d):
     """Training-workload probe scale, rho ~ N(0, 0.1^2): the bf16 bars."""
     say(f"case bwd bf16 B{B} Hq{Hq} Hkv{Hkv} T{T} d{d}")
