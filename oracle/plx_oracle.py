@@ -32,6 +32,19 @@ Backward: the pages give none.  ``row_backward`` is the reverse-mode chain
 rule taken step by step through the explicit forward above (scores ->
 softmax -> moments -> covariance -> output), with rho an independent input.
 
+Family corners (``uniform_weights``, ``row_family``, ``prefill_forward_family``,
+``decode_forward_family``): the unified family ("当注意力学会追问...", section
+2.1) places Parallax at softmax weights + learned probe + intercept and names
+two other axes taken here as switches: the bandwidth axis's far end
+(h -> infinity) gives every key of the set the weight 1/n, and the affine
+axis's no-intercept end sets vbar = kbar = 0, so the covariance becomes the
+uncentred second moment sum_j w_j v_j k_j^T and o = -Sigma rho (with uniform
+weights: causal linear attention with query -rho and 1/n normalisation).
+The correction-to-output ratio (the COR the technical summary tracks,
+section "Risultati Sperimentali", and the metric of "Внимание нового
+поколения...", section "Анализ Parallax: Выводы из внутренних метрик") is read
+as ||Sigma_KV rho||_2 / ||o||_2 per query, Euclidean norms over d_v.
+
 All arithmetic is float64 on the exact (already dtype-rounded) inputs.  The
 per-row functions only use +, -, *, @ and sums once the weights are known, so
 ``row_from_weights`` also runs on numpy object arrays of ``fractions.Fraction``
@@ -52,6 +65,11 @@ __all__ = [
     "row_backward",
     "prefill_backward",
     "prefill_backward_kv_rows",
+    "uniform_weights",
+    "row_family",
+    "correction_to_output",
+    "prefill_forward_family",
+    "decode_forward_family",
 ]
 
 
@@ -235,3 +253,81 @@ def prefill_backward_kv_rows(get_row, keys, T, Hq, Hkv, scale):
         dks.append(acc_k)
         dvs.append(acc_v)
     return np.array(dks), np.array(dvs)
+
+
+# -- family corners and the correction-to-output ratio -------------------------
+
+
+def uniform_weights(n):
+    """Weights at the far end of the bandwidth axis: 1/n on each of the n keys.
+    The LSE reported with them is ln n (every unnormalised weight is one)."""
+    return np.full(n, 1.0 / n), np.log(n)
+
+
+def row_family(w, K, V, rho, intercept=True):
+    """Output and probe correction of one query for a corner of the family.
+
+    intercept=True: the weighted moments are centred (the Parallax form),
+    o = vbar - Sigma rho with Sigma the covariance of ``row_from_weights``.
+    intercept=False: vbar = kbar = 0, Sigma = sum_j w_j v_j k_j^T and
+    o = -Sigma rho.  Returns (o, corr) with corr = Sigma @ rho.
+    Uses only +, -, * and @, so it runs on Fraction object arrays too.
+    """
+    if intercept:
+        o, vbar, _kbar, sigma = row_from_weights(w, K, V, rho)
+    else:
+        sigma = (V * w[:, None]).T @ K  # sum_j w_j v_j k_j^T
+        o = -(sigma @ rho)
+    return o, sigma @ rho
+
+
+def correction_to_output(corr, o):
+    """||corr||_2 / ||o||_2 (IEEE: inf or nan when o = 0)."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.float64(np.linalg.norm(corr)) / np.float64(np.linalg.norm(o))
+
+
+def _family_row(q, K, V, rho, scale, uniform, intercept):
+    if uniform:
+        w, lse = uniform_weights(K.shape[0])
+    else:
+        w, lse = softmax_weights(scale * (K @ q))
+    o, corr = row_family(w, K, V, rho, intercept)
+    return o, lse, correction_to_output(corr, o)
+
+
+def prefill_forward_family(q, k, v, rho, scale, uniform=False, intercept=True):
+    """Causal prefill at a corner of the family.  Shapes as ``prefill_forward``.
+    Returns dict(o, lse, cor); cor is [B, Hq, T]."""
+    B, Hq, T, _ = q.shape
+    Hkv = k.shape[1]
+    o = np.empty((B, Hq, T, v.shape[-1]))
+    lse = np.empty((B, Hq, T))
+    cor = np.empty((B, Hq, T))
+    for b in range(B):
+        for h in range(Hq):
+            hk = _kv_head(h, Hq, Hkv)
+            for i in range(T):
+                o[b, h, i], lse[b, h, i], cor[b, h, i] = _family_row(
+                    q[b, h, i], k[b, hk, : i + 1], v[b, hk, : i + 1], rho[b, h, i], scale,
+                    uniform, intercept)
+    return {"o": o, "lse": lse, "cor": cor}
+
+
+def decode_forward_family(q, rho, k_cache, v_cache, ctx_len, scale, uniform=False,
+                          intercept=True):
+    """Decode at a corner of the family: q, rho [B, Hq, d]; caches
+    [B, Hkv, S_max, d].  Returns dict(o [B, Hq, d], lse [B, Hq], cor [B, Hq])."""
+    B, Hq, _ = q.shape
+    Hkv = k_cache.shape[1]
+    o = np.empty((B, Hq, v_cache.shape[-1]))
+    lse = np.empty((B, Hq))
+    cor = np.empty((B, Hq))
+    for b in range(B):
+        n = int(ctx_len[b])
+        for h in range(Hq):
+            hk = _kv_head(h, Hq, Hkv)
+            o[b, h], lse[b, h], cor[b, h] = _family_row(
+                q[b, h], k_cache[b, hk, :n], v_cache[b, hk, :n], rho[b, h], scale, uniform,
+                intercept)
+    return {"o": o, "lse": lse, "cor": cor}

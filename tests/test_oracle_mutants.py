@@ -92,3 +92,106 @@ def test_pins_catch_mutant(mutant, monkeypatch):
 def test_unmutated_oracle_passes_every_forward_pin():
     for fn, args in _forward_pins():
         fn(*args)
+
+
+# -- family corners and the correction-to-output ratio -------------------------
+
+from tests import test_oracle_family_pins as fpins  # noqa: E402
+
+_row_family = orc.row_family
+_uniform_weights = orc.uniform_weights
+_cor = orc.correction_to_output
+
+
+def _fm_noint_centred(w, K, V, rho, intercept=True):
+    if intercept:
+        return _row_family(w, K, V, rho, True)
+    vbar, kbar = w @ V, w @ K
+    sigma = ((V - vbar) * w[:, None]).T @ (K - kbar)
+    return -(sigma @ rho), sigma @ rho
+
+
+def _fm_noint_sign(w, K, V, rho, intercept=True):
+    if intercept:
+        return _row_family(w, K, V, rho, True)
+    sigma = (V * w[:, None]).T @ K
+    return sigma @ rho, sigma @ rho
+
+
+def _fm_noint_transposed(w, K, V, rho, intercept=True):
+    if intercept:
+        return _row_family(w, K, V, rho, True)
+    sigma = (K * w[:, None]).T @ V  # d_k x d_v: sum_j w_j k_j (v_j . rho)
+    return -(sigma @ rho), sigma @ rho
+
+
+def _fm_noint_keeps_vbar(w, K, V, rho, intercept=True):
+    if intercept:
+        return _row_family(w, K, V, rho, True)
+    sigma = (V * w[:, None]).T @ K
+    return w @ V - sigma @ rho, sigma @ rho
+
+
+def _fm_corr_is_output(w, K, V, rho, intercept=True):
+    o, _ = _row_family(w, K, V, rho, intercept)
+    return o, o
+
+
+def _fm_uniform_n_minus_1(n):
+    m = max(n - 1, 1)
+    return np.full(n, 1.0 / m), np.log(m)
+
+
+def _fm_uniform_lse_zero(n):
+    return np.full(n, 1.0 / n), 0.0
+
+
+def _fm_cor_squared(corr, o):
+    return np.float64(np.dot(corr, corr)) / np.float64(np.dot(o, o))
+
+
+def _fm_cor_inverted(corr, o):
+    return np.float64(np.linalg.norm(o)) / np.float64(np.linalg.norm(corr))
+
+
+FAMILY_MUTANTS = [
+    ("row_family", _fm_noint_centred), ("row_family", _fm_noint_sign),
+    ("row_family", _fm_noint_transposed), ("row_family", _fm_noint_keeps_vbar),
+    ("row_family", _fm_corr_is_output), ("uniform_weights", _fm_uniform_n_minus_1),
+    ("uniform_weights", _fm_uniform_lse_zero), ("correction_to_output", _fm_cor_squared),
+    ("correction_to_output", _fm_cor_inverted),
+]
+
+
+def _family_pins():
+    for name in dir(fpins):
+        if name.startswith("test_"):
+            fn = getattr(fpins, name)
+            marks = getattr(fn, "pytestmark", [])
+            params = [m for m in marks if m.name == "parametrize"]
+            if params:
+                for args in params[0].args[1]:
+                    yield fn, tuple(args)
+            else:
+                yield fn, ()
+
+
+@pytest.mark.parametrize("target,mutant", FAMILY_MUTANTS, ids=lambda x: x if isinstance(x, str) else x.__name__)
+def test_family_pins_catch_mutant(target, mutant, monkeypatch):
+    monkeypatch.setattr(orc, target, mutant)
+    caught = []
+    with np.errstate(all="ignore"):
+        for fn, args in _family_pins():
+            try:
+                fn(*args)
+            except Exception:
+                caught.append(fn.__name__)
+    assert caught, f"no pin caught {mutant.__name__}"
+
+
+def test_unmutated_oracle_passes_every_family_pin():
+    n = 0
+    for fn, args in _family_pins():
+        fn(*args)
+        n += 1
+    assert n >= 12
