@@ -140,6 +140,50 @@ plx_status plx_decode(const void* q, const void* rho, const void* k_cache, const
                       void* workspace, size_t workspace_bytes, plx_dtype dtype, plx_stream stream);
 
 /*
+ * Family corners and the correction-to-output ratio.
+ *
+ * The pages place Parallax in a family of attention operators spanned by three
+ * axes ("当注意力学会追问..." (zhichai.net), section 2.1): the bandwidth (softmax
+ * weights at a finite temperature, or uniform weights in the h -> infinity
+ * limit), the probe, and the affine structure (with an intercept, keeping vbar,
+ * or without one, vbar = kbar = 0 as in linear attention).  The _ex entry
+ * points take the two switchable axes as flags; flags = 0 is exactly
+ * plx_fwd_prefill / plx_decode:
+ *   PLX_UNIFORM_WEIGHTS  w_ij = 1/n_i over the key set of query i (the scores
+ *                        are not used; the probe scores r_ij still are).  The
+ *                        LSE output is then ln n_i.  K must be finite.
+ *   PLX_NO_INTERCEPT     vbar = kbar = 0 in the covariance:
+ *                        Sigma^(i) = sum_j w_ij v_j k_j^T (uncentred) and
+ *                        o_i = -Sigma^(i) rho_i.
+ * Both flags together give causal linear attention with query -rho_i and 1/n_i
+ * normalisation.
+ *
+ *   cor   [B, Hq, T] (prefill) or [B, Hq] (decode) fp32, or NULL: the
+ *         correction-to-output ratio ||Sigma^(i) rho_i||_2 / ||o_i||_2 per
+ *         query, the diagnostic the technical summary ("Riepilogo Tecnico:
+ *         Parallax ...", section "Risultati Sperimentali") and "Внимание
+ *         нового поколения: локальная линейная модель Parallax ..." (section
+ *         "Анализ Parallax: Выводы из внутренних метрик") track; the norms are
+ *         read as Euclidean over d.  It is 0 for a single key with an intercept and
+ *         1 without an intercept; IEEE inf / NaN when o_i = 0.
+ * c_aux and vbar_aux keep their meaning (C/l and O/l, the softmax- or
+ * uniformly-weighted means) at every corner; plx_bwd differentiates the
+ * flags = 0 operator only.  Every other argument, layout rule and error is as
+ * in plx_fwd_prefill / plx_decode; unknown flag bits return PLX_ERR_INVALID_ARG.
+ */
+#define PLX_UNIFORM_WEIGHTS 1u
+#define PLX_NO_INTERCEPT 2u
+plx_status plx_fwd_prefill_ex(const void* q, const void* k, const void* v, const void* rho,
+                              float* o, float* lse, float* c_aux, float* vbar_aux, float* cor,
+                              int B, int Hq, int Hkv, int T, int d, float scale, unsigned flags,
+                              plx_dtype dtype, plx_stream stream);
+plx_status plx_decode_ex(const void* q, const void* rho, const void* k_cache, const void* v_cache,
+                         const int32_t* ctx_len, float* o, float* lse, float* cor, int B, int Hq,
+                         int Hkv, int S_max, int d, float scale, int num_splits, unsigned flags,
+                         void* workspace, size_t workspace_bytes, plx_dtype dtype,
+                         plx_stream stream);
+
+/*
  * Backward of the causal prefill (the pages give none; these are the exact
  * gradients of the forward above with rho an independent input).
  *

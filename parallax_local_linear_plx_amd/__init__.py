@@ -5,12 +5,16 @@ this package only loads it and marshals torch tensors into its calls.
 """
 
 from .binding import (  # noqa: F401
+    PLX_NO_INTERCEPT,
+    PLX_UNIFORM_WEIGHTS,
     PlxError,
     bwd_workspace_size,
     decode_workspace_size,
     lib,
     plx_bwd,
     plx_decode,
+    plx_decode_ex,
     plx_fwd_prefill,
+    plx_fwd_prefill_ex,
     status_string,
 )

@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(PKG, "libplx.so")
 
 PLX_OK, PLX_ERR_INVALID_ARG, PLX_ERR_UNSUPPORTED, PLX_ERR_WORKSPACE, PLX_ERR_HIP = range(5)
 PLX_F32, PLX_BF16 = 0, 1
+# family-corner flags of the _ex entry points
+PLX_UNIFORM_WEIGHTS, PLX_NO_INTERCEPT = 1, 2
 
 _lib = None
 
@@ -47,6 +49,12 @@ def lib() -> ctypes.CDLL:
     L.plx_fwd_prefill.restype = _i
     L.plx_fwd_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _i, _i, _i, _i, _i, _f, _i, _vp]
+    L.plx_fwd_prefill_ex.restype = _i
+    L.plx_fwd_prefill_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _i, _i, _i, _i, _i, _f, ctypes.c_uint, _i, _vp]
+    L.plx_decode_ex.restype = _i
+    L.plx_decode_ex.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _i, _i, _i, _i, _i, _f, _i, ctypes.c_uint, _vp, _sz, _i, _vp]
     L.plx_decode_workspace_size.restype = _sz
     L.plx_decode_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
     L.plx_decode.restype = _i
@@ -116,6 +124,18 @@ def plx_fwd_prefill(q, k, v, rho, scale=None, *, o=None, lse=True, aux=False):
     Returns dict with o [B,Hq,T,d] fp32, and lse [B,Hq,T] when ``lse``; with
     ``aux`` also c [B,Hq,T] and vbar [B,Hq,T,d] (the backward's auxiliaries).
     """
+    return _prefill(q, k, v, rho, scale, o=o, lse=lse, aux=aux, ex=None)
+
+
+def plx_fwd_prefill_ex(q, k, v, rho, scale=None, *, flags=0, cor=True, o=None, lse=True,
+                       aux=False):
+    """Prefill at a corner of the family (``flags``: PLX_UNIFORM_WEIGHTS |
+    PLX_NO_INTERCEPT); with ``cor`` the result also holds cor [B,Hq,T], the
+    correction-to-output ratio.  Otherwise as ``plx_fwd_prefill``."""
+    return _prefill(q, k, v, rho, scale, o=o, lse=lse, aux=aux, ex=(int(flags), bool(cor)))
+
+
+def _prefill(q, k, v, rho, scale, *, o, lse, aux, ex):
     torch = _torch()
     B, Hq, T, d = q.shape
     Hkv = k.shape[1]
@@ -131,10 +151,20 @@ def plx_fwd_prefill(q, k, v, rho, scale=None, *, o=None, lse=True, aux=False):
     lse_t = torch.empty((B, Hq, T), dtype=torch.float32, device=dev) if (lse or aux) else None
     c_t = torch.empty((B, Hq, T), dtype=torch.float32, device=dev) if aux else None
     vb_t = torch.empty((B, Hq, T, d), dtype=torch.float32, device=dev) if aux else None
-    st = lib().plx_fwd_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(o), _ptr(lse_t),
-                               _ptr(c_t), _ptr(vb_t), B, Hq, Hkv, T, d, float(scale),
-                               _dtype_code(q), _stream(dev))
-    _check(st, "plx_fwd_prefill")
+    if ex is None:
+        st = lib().plx_fwd_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(o), _ptr(lse_t),
+                                   _ptr(c_t), _ptr(vb_t), B, Hq, Hkv, T, d, float(scale),
+                                   _dtype_code(q), _stream(dev))
+        _check(st, "plx_fwd_prefill")
+    else:
+        flags, want_cor = ex
+        cor_t = torch.empty((B, Hq, T), dtype=torch.float32, device=dev) if want_cor else None
+        st = lib().plx_fwd_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(rho), _ptr(o), _ptr(lse_t),
+                                      _ptr(c_t), _ptr(vb_t), _ptr(cor_t), B, Hq, Hkv, T, d,
+                                      float(scale), flags, _dtype_code(q), _stream(dev))
+        _check(st, "plx_fwd_prefill_ex")
+        if cor_t is not None:
+            out["cor"] = cor_t
     if lse_t is not None:
         out["lse"] = lse_t
     if aux:
@@ -150,6 +180,19 @@ def decode_workspace_size(B, Hq, Hkv, S_max, d, num_splits=0) -> int:
 def plx_decode(q, rho, k_cache, v_cache, ctx_len, scale=None, *, num_splits=0, workspace=None,
                o=None, lse=True):
     """Decode.  q, rho [B,Hq,d]; caches [B,Hkv,S_max,d]; ctx_len int32 [B] on the device."""
+    return _decode(q, rho, k_cache, v_cache, ctx_len, scale, num_splits=num_splits,
+                   workspace=workspace, o=o, lse=lse, ex=None)
+
+
+def plx_decode_ex(q, rho, k_cache, v_cache, ctx_len, scale=None, *, flags=0, cor=True,
+                  num_splits=0, workspace=None, o=None, lse=True):
+    """Decode at a corner of the family; with ``cor`` the result also holds
+    cor [B,Hq].  Otherwise as ``plx_decode``."""
+    return _decode(q, rho, k_cache, v_cache, ctx_len, scale, num_splits=num_splits,
+                   workspace=workspace, o=o, lse=lse, ex=(int(flags), bool(cor)))
+
+
+def _decode(q, rho, k_cache, v_cache, ctx_len, scale, *, num_splits, workspace, o, lse, ex):
     torch = _torch()
     B, Hq, d = q.shape
     Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
@@ -166,12 +209,24 @@ def plx_decode(q, rho, k_cache, v_cache, ctx_len, scale=None, *, num_splits=0, w
     if o is None:
         o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     lse_t = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse else None
-    st = lib().plx_decode(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len), _ptr(o),
-                          _ptr(lse_t), B, Hq, Hkv, S_max, d, float(scale), int(num_splits),
-                          _ptr(workspace), workspace.numel() * workspace.element_size(),
-                          _dtype_code(q), _stream(dev))
-    _check(st, "plx_decode")
+    ws_bytes = workspace.numel() * workspace.element_size()
     out = {"o": o}
+    if ex is None:
+        st = lib().plx_decode(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len),
+                              _ptr(o), _ptr(lse_t), B, Hq, Hkv, S_max, d, float(scale),
+                              int(num_splits), _ptr(workspace), ws_bytes, _dtype_code(q),
+                              _stream(dev))
+        _check(st, "plx_decode")
+    else:
+        flags, want_cor = ex
+        cor_t = torch.empty((B, Hq), dtype=torch.float32, device=dev) if want_cor else None
+        st = lib().plx_decode_ex(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len),
+                                 _ptr(o), _ptr(lse_t), _ptr(cor_t), B, Hq, Hkv, S_max, d,
+                                 float(scale), int(num_splits), flags, _ptr(workspace), ws_bytes,
+                                 _dtype_code(q), _stream(dev))
+        _check(st, "plx_decode_ex")
+        if cor_t is not None:
+            out["cor"] = cor_t
     if lse_t is not None:
         out["lse"] = lse_t
     return out

@@ -10,6 +10,9 @@
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }  // NULL passes
+
+bool flags_ok(unsigned f) { return (f & ~(PLX_UNIFORM_WEIGHTS | PLX_NO_INTERCEPT)) == 0; }
 
 bool dtype_ok(plx_dtype dt) { return dt == PLX_F32 || dt == PLX_BF16; }
 
@@ -44,19 +47,27 @@ const char* plx_status_string(plx_status s) {
   return "unknown status";
 }
 
-plx_status plx_fwd_prefill(const void* q, const void* k, const void* v, const void* rho, float* o,
-                           float* lse, float* c_aux, float* vbar_aux, int B, int Hq, int Hkv, int T,
-                           int d, float scale, plx_dtype dtype, plx_stream stream) {
+plx_status plx_fwd_prefill_ex(const void* q, const void* k, const void* v, const void* rho,
+                              float* o, float* lse, float* c_aux, float* vbar_aux, float* cor,
+                              int B, int Hq, int Hkv, int T, int d, float scale, unsigned flags,
+                              plx_dtype dtype, plx_stream stream) {
   if (!q || !k || !v || !rho || !o) return PLX_ERR_INVALID_ARG;
-  if (!dtype_ok(dtype) || T < 1 || !scale_ok(scale)) return PLX_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype) || T < 1 || !scale_ok(scale) || !flags_ok(flags)) return PLX_ERR_INVALID_ARG;
   plx_status st = check_heads(B, Hq, Hkv, d);
   if (st != PLX_OK) return st;
   if (!size_ok((long long)B * Hq * T, d)) return PLX_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rho) || !aligned16(o) ||
-      (vbar_aux && !aligned16(vbar_aux)))
+      (vbar_aux && !aligned16(vbar_aux)) || !aligned4(lse) || !aligned4(c_aux) || !aligned4(cor))
     return PLX_ERR_INVALID_ARG;
-  return from_hip(plx::launch_fwd(dtype, q, k, v, rho, o, lse, c_aux, vbar_aux, B, Hq, Hkv, T, d,
-                                  scale, (hipStream_t)stream));
+  return from_hip(plx::launch_fwd(dtype, q, k, v, rho, o, lse, c_aux, vbar_aux, cor, flags, B, Hq,
+                                  Hkv, T, d, scale, (hipStream_t)stream));
+}
+
+plx_status plx_fwd_prefill(const void* q, const void* k, const void* v, const void* rho, float* o,
+                           float* lse, float* c_aux, float* vbar_aux, int B, int Hq, int Hkv, int T,
+                           int d, float scale, plx_dtype dtype, plx_stream stream) {
+  return plx_fwd_prefill_ex(q, k, v, rho, o, lse, c_aux, vbar_aux, nullptr, B, Hq, Hkv, T, d, scale,
+                            0u, dtype, stream);
 }
 
 size_t plx_decode_workspace_size(int B, int Hq, int Hkv, int S_max, int d, int num_splits) {
@@ -76,25 +87,36 @@ size_t plx_decode_workspace_size(int B, int Hq, int Hkv, int S_max, int d, int n
   return bytes;
 }
 
-plx_status plx_decode(const void* q, const void* rho, const void* k_cache, const void* v_cache,
-                      const int32_t* ctx_len, float* o, float* lse, int B, int Hq, int Hkv,
-                      int S_max, int d, float scale, int num_splits, void* workspace,
-                      size_t workspace_bytes, plx_dtype dtype, plx_stream stream) {
+plx_status plx_decode_ex(const void* q, const void* rho, const void* k_cache, const void* v_cache,
+                         const int32_t* ctx_len, float* o, float* lse, float* cor, int B, int Hq,
+                         int Hkv, int S_max, int d, float scale, int num_splits, unsigned flags,
+                         void* workspace, size_t workspace_bytes, plx_dtype dtype,
+                         plx_stream stream) {
   if (!q || !rho || !k_cache || !v_cache || !ctx_len || !o) return PLX_ERR_INVALID_ARG;
-  if (!dtype_ok(dtype) || S_max < 1 || num_splits < 0 || !scale_ok(scale)) return PLX_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype) || S_max < 1 || num_splits < 0 || !scale_ok(scale) || !flags_ok(flags))
+    return PLX_ERR_INVALID_ARG;
   plx_status st = check_heads(B, Hq, Hkv, d);
   if (st != PLX_OK) return st;
   const int group = Hq / Hkv;
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return PLX_ERR_UNSUPPORTED;
   if (!size_ok((long long)B * Hkv * S_max, d)) return PLX_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(rho) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned16(o) || (workspace && !aligned16(workspace)))
+      !aligned16(o) || (workspace && !aligned16(workspace)) || !aligned4(ctx_len) || !aligned4(lse) ||
+      !aligned4(cor))
     return PLX_ERR_INVALID_ARG;
   const size_t need = plx_decode_workspace_size(B, Hq, Hkv, S_max, d, num_splits);
   if (!workspace || workspace_bytes < need) return PLX_ERR_WORKSPACE;
-  return from_hip(plx::launch_decode(dtype, q, rho, k_cache, v_cache, ctx_len, o, lse, B, Hq, Hkv,
-                                     S_max, d, scale, num_splits, (float*)workspace,
+  return from_hip(plx::launch_decode(dtype, q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B,
+                                     Hq, Hkv, S_max, d, scale, num_splits, (float*)workspace,
                                      (hipStream_t)stream));
+}
+
+plx_status plx_decode(const void* q, const void* rho, const void* k_cache, const void* v_cache,
+                      const int32_t* ctx_len, float* o, float* lse, int B, int Hq, int Hkv,
+                      int S_max, int d, float scale, int num_splits, void* workspace,
+                      size_t workspace_bytes, plx_dtype dtype, plx_stream stream) {
+  return plx_decode_ex(q, rho, k_cache, v_cache, ctx_len, o, lse, nullptr, B, Hq, Hkv, S_max, d,
+                       scale, num_splits, 0u, workspace, workspace_bytes, dtype, stream);
 }
 
 size_t plx_bwd_workspace_size(int B, int Hq, int Hkv, int T, int d) {

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
     const typename Pol::in_t* __restrict__ q, const typename Pol::in_t* __restrict__ rho,
     const typename Pol::in_t* __restrict__ kc, const typename Pol::in_t* __restrict__ vc,
     const int32_t* __restrict__ ctx_len, float* __restrict__ part, int Hkv, int S_max, int chunk,
-    int nsplit, float scale_log2) {
+    int nsplit, unsigned flags, float scale_log2) {
   using in_t = typename Pol::in_t;
   using sop_t = typename Pol::sop_t;
   using vop_t = typename Pol::vop_t;
@@ -86,15 +86,17 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
   const int col = lane & 31, half = lane >> 5;
   const int Hq = Hkv * G;
 
-  // B operand: column c -> q (even) or rho (odd) of head hk*G + c/2
+  // B operand: column c -> q (even) or rho (odd) of head hk*G + c/2; with
+  // uniform weights the q columns are zero (every score exactly 0, p = 1)
   sop_t bop[NS];
   {
     const int hq = hk * G + (col >> 1);
     const in_t* src = (col & 1) ? rho : q;
+    const bool load = col < 2 * G && ((col & 1) || !(flags & PLX_UNIFORM_WEIGHTS));
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      bop[s] = (col < 2 * G) ? load_sop<Pol>(src + ((size_t)b * Hq + hq) * D + KSTEP * s + KW * half)
-                             : zero_sop<Pol>();
+      bop[s] = load ? load_sop<Pol>(src + ((size_t)b * Hq + hq) * D + KSTEP * s + KW * half)
+                    : zero_sop<Pol>();
   }
 
   const in_t* kbase = kc + ((size_t)(b * Hkv + hk) * S_max) * D;
@@ -347,7 +349,8 @@ __device__ __forceinline__ void dec16_range(Dec16Smem<D>& sm, const uint16_t* __
                                             const uint16_t* __restrict__ kc,
                                             const uint16_t* __restrict__ vc, int b, int hk, int hq0,
                                             int Hq, int Hkv, int S_max, int k_begin, int k_end,
-                                            float scale_log2, float* __restrict__ rec, size_t rec_stride) {
+                                            unsigned flags, float scale_log2, float* __restrict__ rec,
+                                            size_t rec_stride) {
   constexpr int NS = D / 32;  // 32-deep score steps
   constexpr int ND = D / 16;  // 16-row d tiles of the value accumulators
   using SM = Dec16Smem<D>;
@@ -356,11 +359,13 @@ __device__ __forceinline__ void dec16_range(Dec16Smem<D>& sm, const uint16_t* __
   const int c = lane & 15, g = lane >> 4;
 
   // B operand of the score MFMAs, staged once in LDS: column cc holds q (even)
-  // or rho (odd) of head hq0 + cc/2 (zero for unused columns)
+  // or rho (odd) of head hq0 + cc/2 (zero for unused columns, and for the q
+  // columns with uniform weights: every score is then exactly 0, p = 1)
+  const bool use_q = !(flags & PLX_UNIFORM_WEIGHTS);
   for (int i = threadIdx.x; i < 16 * D / 8; i += DEC_THREADS) {
     const int cc = i / (D / 8), d0 = (i % (D / 8)) * 8;
     u32x4 raw = {0u, 0u, 0u, 0u};
-    if (cc < 2 * G) {
+    if (cc < 2 * G && ((cc & 1) || use_q)) {
       const uint16_t* src = (cc & 1) ? rho : q;
       raw = *reinterpret_cast<const u32x4*>(src + ((size_t)b * Hq + hq0 + (cc >> 1)) * D + d0);
     }
@@ -545,7 +550,7 @@ template <int D, int G>
 __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ rho, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ ctx_len, float* __restrict__ part,
-    int Hq, int Hkv, int S_max, int chunk, int nsplit, int hoff, float scale_log2) {
+    int Hq, int Hkv, int S_max, int chunk, int nsplit, int hoff, unsigned flags, float scale_log2) {
   constexpr int REC = 2 * D + 4;
   __shared__ Dec16Smem<D> sm;
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -555,19 +560,21 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_chunk_kernel(
   const int k_end = min(ctx, k_begin + chunk);
   const int hq0 = hk * (Hq / Hkv) + hoff;
   float* rec = part + (((size_t)b * Hq + hq0) * nsplit + split) * REC;
-  dec16_range<D, G>(sm, q, rho, kc, vc, b, hk, hq0, Hq, Hkv, S_max, k_begin, k_end, scale_log2, rec,
-                    (size_t)nsplit * REC);
+  dec16_range<D, G>(sm, q, rho, kc, vc, b, hk, hq0, Hq, Hkv, S_max, k_begin, k_end, flags,
+                    scale_log2, rec, (size_t)nsplit * REC);
 }
 
 // One wave merges the n records of one head (record i at rec0 + i * stride;
 // a record with valid(i) false was never written and is skipped) into
-//   o = (O/l)(1 + C/l) - U/l,   LSE = M + ln e   (natural log).
+//   o = (O/l)(1 + C/l) - U/l   (without an intercept: o = -U/l),
+//   LSE = M + ln e   (natural log),
+//   COR = ||U/l - (O/l)(C/l)|| / ||o||   (without an intercept: ||U/l|| / ||o||).
 // Lane j holds elements j * D/64 ..; every record's O and U loads are issued
 // unconditionally (the slots lie inside the workspace) so that they overlap.
 template <int D, class Valid>
 __device__ __forceinline__ void wave_merge(const float* __restrict__ rec0, size_t stride, int n,
-                                           Valid valid, float* __restrict__ orow,
-                                           float* __restrict__ lse_out) {
+                                           Valid valid, unsigned flags, float* __restrict__ orow,
+                                           float* __restrict__ lse_out, float* __restrict__ cor_out) {
   constexpr int EPL = D / 64;
   const int lane = threadIdx.x & 63;
   float M = -INFINITY;
@@ -623,16 +630,34 @@ __device__ __forceinline__ void wave_merge(const float* __restrict__ rec0, size_
     C += __shfl_xor(C, off, 64);
   }
   const float inv = 1.f / l;
+  const float cc = C * inv;
+  const bool no_icpt = flags & PLX_NO_INTERCEPT;
+  float n_o = 0.f, n_c = 0.f;
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) orow[lane * EPL + j] = O[j] * inv * (1.f + C * inv) - U[j] * inv;
+  for (int j = 0; j < EPL; ++j) {
+    const float vbar = O[j] * inv, u = U[j] * inv;
+    const float ov = no_icpt ? -u : vbar * (1.f + cc) - u;
+    const float corr = no_icpt ? u : u - vbar * cc;
+    orow[lane * EPL + j] = ov;
+    n_o = __builtin_fmaf(ov, ov, n_o);
+    n_c = __builtin_fmaf(corr, corr, n_c);
+  }
   if (lse_out && lane == 0) *lse_out = (M + __log2f(e)) * kLn2;
+  if (cor_out) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      n_o += __shfl_xor(n_o, off, 64);
+      n_c += __shfl_xor(n_c, off, 64);
+    }
+    if (lane == 0) *cor_out = __builtin_sqrtf(n_c) / __builtin_sqrtf(n_o);
+  }
 }
 
 template <int D, int G>
 __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_balanced_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ rho, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ ctx_len, float* __restrict__ part,
-    int B, int Hq, int Hkv, int S_max, int hoff, float scale_log2) {
+    int B, int Hq, int Hkv, int S_max, int hoff, unsigned flags, float scale_log2) {
   constexpr int REC = 2 * D + 4;
   __shared__ Dec16Smem<D> sm;
   const int lane = threadIdx.x & 63;
@@ -677,7 +702,8 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_balanced_kernel(
     const int hq0 = hk * Gfull + hoff;
     const long long seg = (long long)b * Hkv + hk;
     float* rec = part + ((size_t)(blockIdx.x + seg) * Gfull + hoff) * REC;
-    dec16_range<D, G>(sm, q, rho, kc, vc, b, hk, hq0, Hq, Hkv, S_max, key, k_end, scale_log2, rec, REC);
+    dec16_range<D, G>(sm, q, rho, kc, vc, b, hk, hq0, Hq, Hkv, S_max, key, k_end, flags, scale_log2,
+                      rec, REC);
     pos += k_end - key;
     if (pos >= hi) break;
     key = 0;
@@ -694,16 +720,17 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_balanced_kernel(
 template <int D, int G>
 hipError_t launch_partial16(const void* q, const void* rho, const void* kc, const void* vc,
                             const int32_t* ctx_len, float* part, int B, int Hq, int Hkv, int S_max,
-                            int chunk, int nsplit, int hoff, float scale, hipStream_t stream) {
+                            int chunk, int nsplit, int hoff, unsigned flags, float scale,
+                            hipStream_t stream) {
   if (chunk <= 0) {
     hipLaunchKernelGGL((decode16_balanced_kernel<D, G>), dim3(nsplit), dim3(DEC_THREADS), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)rho, (const uint16_t*)kc, (const uint16_t*)vc,
-                       ctx_len, part, B, Hq, Hkv, S_max, hoff, scale * kLog2e);
+                       ctx_len, part, B, Hq, Hkv, S_max, hoff, flags, scale * kLog2e);
   } else {
     dim3 grid(nsplit, Hkv, B);
     hipLaunchKernelGGL((decode16_chunk_kernel<D, G>), grid, dim3(DEC_THREADS), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)rho, (const uint16_t*)kc, (const uint16_t*)vc,
-                       ctx_len, part, Hq, Hkv, S_max, chunk, nsplit, hoff, scale * kLog2e);
+                       ctx_len, part, Hq, Hkv, S_max, chunk, nsplit, hoff, flags, scale * kLog2e);
   }
   return hipGetLastError();
 }
@@ -714,6 +741,7 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_merge_chunk_kernel(const float* __restrict__ part,
                                                                  const int32_t* __restrict__ ctx_len,
                                                                  float* __restrict__ o, float* __restrict__ lse,
+                                                                 float* __restrict__ cor, unsigned flags,
                                                                  int B, int Hq, int S_max, int chunk, int nsplit) {
   constexpr int REC = 2 * D + 4;
   const int lane = threadIdx.x & 63;
@@ -722,13 +750,18 @@ __global__ __launch_bounds__(256) void decode_merge_chunk_kernel(const float* __
   const int ctx = dec_len(ctx_len, bh / Hq, S_max);
   float* orow = o + (size_t)bh * D;
   float* lse_out = lse ? lse + bh : nullptr;
+  float* cor_out = cor ? cor + bh : nullptr;
   if (ctx == 0) {
     for (int i = lane; i < D; i += 64) orow[i] = __builtin_nanf("");
-    if (lse_out && lane == 0) *lse_out = __builtin_nanf("");
+    if (lane == 0) {
+      if (lse_out) *lse_out = __builtin_nanf("");
+      if (cor_out) *cor_out = __builtin_nanf("");
+    }
     return;
   }
   const int n = (ctx + chunk - 1) / chunk;
-  wave_merge<D>(part + (size_t)bh * nsplit * REC, REC, n, [](int) { return true; }, orow, lse_out);
+  wave_merge<D>(part + (size_t)bh * nsplit * REC, REC, n, [](int) { return true; }, flags, orow,
+                lse_out, cor_out);
 }
 
 // Balanced schedule: segment s = b * Hkv + h / G covers keys [start, end) of
@@ -739,6 +772,7 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_merge_balanced_kernel(const float* __restrict__ part,
                                                                     const int32_t* __restrict__ ctx_len,
                                                                     float* __restrict__ o, float* __restrict__ lse,
+                                                                    float* __restrict__ cor, unsigned flags,
                                                                     int B, int Hq, int Hkv, int S_max, int P) {
   constexpr int REC = 2 * D + 4;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -748,9 +782,13 @@ __global__ __launch_bounds__(256) void decode_merge_balanced_kernel(const float*
   const int len = dec_len(ctx_len, b, S_max);
   float* orow = o + (size_t)bh * D;
   float* lse_out = lse ? lse + bh : nullptr;
+  float* cor_out = cor ? cor + bh : nullptr;
   if (len == 0) {
     for (int i = lane; i < D; i += 64) orow[i] = __builtin_nanf("");
-    if (lse_out && lane == 0) *lse_out = __builtin_nanf("");
+    if (lane == 0) {
+      if (lse_out) *lse_out = __builtin_nanf("");
+      if (cor_out) *cor_out = __builtin_nanf("");
+    }
     return;
   }
   long long tot = 0, pre = 0;
@@ -768,33 +806,33 @@ __global__ __launch_bounds__(256) void decode_merge_balanced_kernel(const float*
   const long long seg = (long long)b * Hkv + hk;
   wave_merge<D>(part + ((size_t)(w0 + seg) * Gfull + (h % Gfull)) * REC, (size_t)Gfull * REC, n,
                 [&](int i) { return W >= P || bal_lo(w0 + i, W, P) < bal_lo(w0 + i + 1, W, P); },
-                orow, lse_out);
+                flags, orow, lse_out, cor_out);
 }
 
 template <class Pol, int D, int G>
 hipError_t launch_partial(const void* q, const void* rho, const void* kc, const void* vc,
                           const int32_t* ctx_len, float* part, int B, int Hkv, int S_max, int chunk,
-                          int nsplit, float scale, hipStream_t stream) {
+                          int nsplit, unsigned flags, float scale, hipStream_t stream) {
   using in_t = typename Pol::in_t;
   dim3 grid(nsplit, Hkv, B);
   hipLaunchKernelGGL((decode_partial_kernel<Pol, D, G>), grid, dim3(DEC_THREADS), 0, stream,
                      (const in_t*)q, (const in_t*)rho, (const in_t*)kc, (const in_t*)vc, ctx_len, part,
-                     Hkv, S_max, chunk, nsplit, scale * kLog2e);
+                     Hkv, S_max, chunk, nsplit, flags, scale * kLog2e);
   return hipGetLastError();
 }
 
 template <class Pol, int D>
 hipError_t launch_decode_t(const void* q, const void* rho, const void* kc, const void* vc,
-                           const int32_t* ctx_len, float* o, float* lse, int B, int Hq, int Hkv,
-                           int S_max, float scale, int chunk, int nsplit, float* part,
-                           hipStream_t stream) {
+                           const int32_t* ctx_len, float* o, float* lse, float* cor,
+                           unsigned flags, int B, int Hq, int Hkv, int S_max, float scale, int chunk,
+                           int nsplit, float* part, hipStream_t stream) {
   const int G = Hq / Hkv;
   hipError_t e;
   if constexpr (sizeof(typename Pol::in_t) == 2) {
     // bf16: 16-column kernel; 16 heads per KV head take two column groups
 #define PLX_P16(GG, HOFF)                                                                          \
   launch_partial16<D, GG>(q, rho, kc, vc, ctx_len, part, B, Hq, Hkv, S_max, chunk, nsplit, HOFF, \
-                          scale, stream)
+                          flags, scale, stream)
     switch (G) {
       case 1: e = PLX_P16(1, 0); break;
       case 2: e = PLX_P16(2, 0); break;
@@ -809,23 +847,23 @@ hipError_t launch_decode_t(const void* q, const void* rho, const void* kc, const
     if (e != hipSuccess) return e;
     if (chunk <= 0)
       hipLaunchKernelGGL((decode_merge_balanced_kernel<D>), dim3((B * Hq + 3) / 4), dim3(256), 0, stream,
-                         part, ctx_len, o, lse, B, Hq, Hkv, S_max, nsplit);
+                         part, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, nsplit);
     else
       hipLaunchKernelGGL((decode_merge_chunk_kernel<D>), dim3((B * Hq + 3) / 4), dim3(256), 0, stream,
-                         part, ctx_len, o, lse, B, Hq, S_max, chunk, nsplit);
+                         part, ctx_len, o, lse, cor, flags, B, Hq, S_max, chunk, nsplit);
     return hipGetLastError();
   } else {
     // fp32: the generic 32-column kernel (chunked schedule only)
     switch (G) {
-      case 1: e = launch_partial<Pol, D, 1>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
-      case 2: e = launch_partial<Pol, D, 2>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
-      case 4: e = launch_partial<Pol, D, 4>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
-      case 8: e = launch_partial<Pol, D, 8>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
-      default: e = launch_partial<Pol, D, 16>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, scale, stream); break;
+      case 1: e = launch_partial<Pol, D, 1>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, flags, scale, stream); break;
+      case 2: e = launch_partial<Pol, D, 2>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, flags, scale, stream); break;
+      case 4: e = launch_partial<Pol, D, 4>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, flags, scale, stream); break;
+      case 8: e = launch_partial<Pol, D, 8>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, flags, scale, stream); break;
+      default: e = launch_partial<Pol, D, 16>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, flags, scale, stream); break;
     }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge_chunk_kernel<D>), dim3((B * Hq + 3) / 4), dim3(256), 0, stream,
-                       part, ctx_len, o, lse, B, Hq, S_max, chunk, nsplit);
+                       part, ctx_len, o, lse, cor, flags, B, Hq, S_max, chunk, nsplit);
     return hipGetLastError();
   }
 }
@@ -869,15 +907,15 @@ size_t decode_balanced_records(int B, int Hq, int Hkv, int S_max) {
 }
 
 hipError_t launch_decode(int dtype, const void* q, const void* rho, const void* k_cache,
-                         const void* v_cache, const int32_t* ctx_len, float* o, float* lse, int B,
-                         int Hq, int Hkv, int S_max, int d, float scale, int num_splits,
-                         float* partials, hipStream_t stream) {
+                         const void* v_cache, const int32_t* ctx_len, float* o, float* lse,
+                         float* cor, unsigned flags, int B, int Hq, int Hkv, int S_max, int d,
+                         float scale, int num_splits, float* partials, hipStream_t stream) {
   if (dtype == PLX_BF16 && num_splits == 0) {
     // balanced schedule (chunk 0); nsplit carries the workgroup count
     const int P = decode_balanced_ctas(B, Hkv, S_max);
     if (d == 64)
-      return launch_decode_t<PolBF16, 64>(q, rho, k_cache, v_cache, ctx_len, o, lse, B, Hq, Hkv, S_max, scale, 0, P, partials, stream);
-    return launch_decode_t<PolBF16, 128>(q, rho, k_cache, v_cache, ctx_len, o, lse, B, Hq, Hkv, S_max, scale, 0, P, partials, stream);
+      return launch_decode_t<PolBF16, 64>(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, scale, 0, P, partials, stream);
+    return launch_decode_t<PolBF16, 128>(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, scale, 0, P, partials, stream);
   }
   int ns = num_splits > 0 ? num_splits : decode_auto_splits(B, Hkv, S_max);
   if (ns > S_max) ns = S_max;
@@ -885,12 +923,12 @@ hipError_t launch_decode(int dtype, const void* q, const void* rho, const void* 
   const int nsplit = (S_max + chunk - 1) / chunk;
   if (dtype == PLX_BF16) {
     if (d == 64)
-      return launch_decode_t<PolBF16, 64>(q, rho, k_cache, v_cache, ctx_len, o, lse, B, Hq, Hkv, S_max, scale, chunk, nsplit, partials, stream);
-    return launch_decode_t<PolBF16, 128>(q, rho, k_cache, v_cache, ctx_len, o, lse, B, Hq, Hkv, S_max, scale, chunk, nsplit, partials, stream);
+      return launch_decode_t<PolBF16, 64>(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, scale, chunk, nsplit, partials, stream);
+    return launch_decode_t<PolBF16, 128>(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, scale, chunk, nsplit, partials, stream);
   }
   if (d == 64)
-    return launch_decode_t<PolF32, 64>(q, rho, k_cache, v_cache, ctx_len, o, lse, B, Hq, Hkv, S_max, scale, chunk, nsplit, partials, stream);
-  return launch_decode_t<PolF32, 128>(q, rho, k_cache, v_cache, ctx_len, o, lse, B, Hq, Hkv, S_max, scale, chunk, nsplit, partials, stream);
+    return launch_decode_t<PolF32, 64>(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, scale, chunk, nsplit, partials, stream);
+  return launch_decode_t<PolF32, 128>(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, scale, chunk, nsplit, partials, stream);
 }
 
 }  // namespace plx

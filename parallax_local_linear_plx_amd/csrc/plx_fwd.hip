@@ -320,7 +320,8 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     const typename Pol::in_t* __restrict__ q, const typename Pol::in_t* __restrict__ k,
     const typename Pol::in_t* __restrict__ v, const typename Pol::in_t* __restrict__ rho,
     float* __restrict__ o, float* __restrict__ lse, float* __restrict__ c_aux,
-    float* __restrict__ vbar_aux, int B, int Hq, int Hkv, int T, float scale_log2) {
+    float* __restrict__ vbar_aux, float* __restrict__ cor, unsigned flags, int B, int Hq, int Hkv,
+    int T, float scale_log2) {
   using in_t = typename Pol::in_t;
   using sop_t = typename Pol::sop_t;
   constexpr int KW = Pol::KW, KSTEP = Pol::KSTEP;
@@ -364,12 +365,14 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
   gload_k<Pol, D>(pre, kp, 0, T);
   gload_v<Pol, D>(pre, vp, 0, T);
 
-  // Q and rho rows of this lane's query as B operands.
+  // Q and rho rows of this lane's query as B operands (uniform weights: a
+  // zero Q operand, so every score is exactly 0 and every unmasked p is 1).
+  const bool use_q = !(flags & PLX_UNIFORM_WEIGHTS);
   sop_t qop[NS], rop[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     if (my_q < T) {
-      qop[s] = load_sop<Pol>(qp + (size_t)my_q * D + KSTEP * s + KW * half);
+      qop[s] = use_q ? load_sop<Pol>(qp + (size_t)my_q * D + KSTEP * s + KW * half) : zero_sop<Pol>();
       rop[s] = load_sop<Pol>(rp + (size_t)my_q * D + KSTEP * s + KW * half);
     } else {
       qop[s] = zero_sop<Pol>();
@@ -416,12 +419,32 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     __syncthreads();
   }
 
-  // epilogue: o = (O/l)(1 + C/l) - U/l ; LSE = ln sum exp(scaled scores)
+  // epilogue: o = (O/l)(1 + C/l) - U/l (without an intercept: -U/l);
+  // LSE = ln sum exp(scaled scores); COR = ||U/l - (O/l)(C/l)|| / ||o||
+  // (without an intercept the correction is U/l).  The two lanes of one
+  // query (same col, half = 0, 1) hold disjoint halves of its d values.
   const float l_tot = S.l_part + xor32(S.l_part);
   const float c_tot = S.c_part + xor32(S.c_part);
   const float e_tot = S.e_part + xor32(S.e_part);
   const float inv = 1.f / l_tot;
   const float cc = c_tot * inv;
+  const bool no_icpt = flags & PLX_NO_INTERCEPT;
+  float n_o = 0.f, n_c = 0.f;
+  if (cor) {
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int a = 0; a < 16; ++a) {
+        const float vbar = S.oacc[dt][a] * inv;
+        const float u = S.uacc[dt][a] * inv;
+        const float ov = no_icpt ? -u : vbar * (1.f + cc) - u;
+        const float corr = no_icpt ? u : u - vbar * cc;
+        n_o = __builtin_fmaf(ov, ov, n_o);
+        n_c = __builtin_fmaf(corr, corr, n_c);
+      }
+    n_o += xor32(n_o);
+    n_c += xor32(n_c);
+  }
   if (my_q < T) {
     float* orow = o + ((size_t)bh * T + my_q) * D;
     float* vrow = vbar_aux ? vbar_aux + ((size_t)bh * T + my_q) * D : nullptr;
@@ -434,8 +457,9 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const float vbar = S.oacc[dt][4 * i + jj] * inv;
+          const float u = S.uacc[dt][4 * i + jj] * inv;
           vv[jj] = vbar;
-          ov[jj] = vbar * (1.f + cc) - S.uacc[dt][4 * i + jj] * inv;
+          ov[jj] = no_icpt ? -u : vbar * (1.f + cc) - u;
         }
         *reinterpret_cast<f32x4*>(orow + d0) = ov;
         if (vrow) *reinterpret_cast<f32x4*>(vrow + d0) = vv;
@@ -443,6 +467,7 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
     if (half == 0) {
       if (lse) lse[(size_t)bh * T + my_q] = (S.m_run + __log2f(e_tot)) * kLn2;
       if (c_aux) c_aux[(size_t)bh * T + my_q] = cc;
+      if (cor) cor[(size_t)bh * T + my_q] = __builtin_sqrtf(n_c) / __builtin_sqrtf(n_o);
     }
   }
 }
@@ -489,8 +514,8 @@ template <int D, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ rho, float* __restrict__ o, float* __restrict__ lse,
-    float* __restrict__ c_aux, float* __restrict__ vbar_aux, int B, int Hq, int Hkv, int T,
-    float scale_log2) {
+    float* __restrict__ c_aux, float* __restrict__ vbar_aux, float* __restrict__ cor,
+    unsigned flags, int B, int Hq, int Hkv, int T, float scale_log2) {
   constexpr int NT = 64 * NW;       // threads
   constexpr int BR = 16 * NW;       // query rows per workgroup
   constexpr int NS = D / 32;        // score MFMA steps over d
@@ -565,14 +590,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     }
   };
 
-  // prologue: tile 0 -> buffer 0; tile 1 in flight (register set B)
+  // prologue: tile 0 -> buffer 0
   gload(preA, 0);
+  // Uniform weights: a zero query operand makes every score exactly 0, so
+  // every unmasked key gets p = 1 and the running max stays 0.
+  const bool use_q = !(flags & PLX_UNIFORM_WEIGHTS);
   bf16x8 qop[NS], rop[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     u32x4 qa = {0u, 0u, 0u, 0u}, ra = {0u, 0u, 0u, 0u};
     if (my_q < T) {
-      qa = *reinterpret_cast<const u32x4*>(qp + (size_t)my_q * D + 32 * s + 8 * g);
+      if (use_q) qa = *reinterpret_cast<const u32x4*>(qp + (size_t)my_q * D + 32 * s + 8 * g);
       ra = *reinterpret_cast<const u32x4*>(rp + (size_t)my_q * D + 32 * s + 8 * g);
     }
     qop[s] = __builtin_bit_cast(bf16x8, qa);
@@ -727,70 +755,91 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
     if (j + 1 < ntiles) iter(j + 1, 1);
   }
 
-  // epilogue: o = (O/l)(1 + C/l) - U/l; LSE = ln sum exp(scaled scores)
+  // epilogue: o = (O/l)(1 + C/l) - U/l (without an intercept: -U/l);
+  // LSE = ln sum exp(scaled scores); COR = ||U/l - (O/l)(C/l)|| / ||o||
+  // (without an intercept the correction is U/l).  The lanes of one query
+  // (same c, g = 0..3) hold disjoint quarters of its d values.
   const float l_tot = lacc[0], c_tot = cacc[0];
   float e_tot = e_part;
   e_tot += __shfl_xor(e_tot, 16, 64);
   e_tot += __shfl_xor(e_tot, 32, 64);
   const float inv = 1.f / l_tot;
   const float cc = c_tot * inv;
+  const bool no_icpt = flags & PLX_NO_INTERCEPT;
+  f32x4 ov[ND], vv[ND];
+  float n_o = 0.f, n_c = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const float vbar = oacc[dt][jj] * inv;
+      const float u = uacc[dt][jj] * inv;
+      vv[dt][jj] = vbar;
+      ov[dt][jj] = no_icpt ? -u : vbar * (1.f + cc) - u;
+      const float corr = no_icpt ? u : u - vbar * cc;
+      n_o = __builtin_fmaf(ov[dt][jj], ov[dt][jj], n_o);
+      n_c = __builtin_fmaf(corr, corr, n_c);
+    }
+  if (cor) {
+    n_o += __shfl_xor(n_o, 16, 64);
+    n_o += __shfl_xor(n_o, 32, 64);
+    n_c += __shfl_xor(n_c, 16, 64);
+    n_c += __shfl_xor(n_c, 32, 64);
+  }
   if (my_q < T) {
     float* orow = o + ((size_t)bh * T + my_q) * D;
     float* vrow = vbar_aux ? vbar_aux + ((size_t)bh * T + my_q) * D : nullptr;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
-      f32x4 ov, vv;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float vbar = oacc[dt][jj] * inv;
-        vv[jj] = vbar;
-        ov[jj] = vbar * (1.f + cc) - uacc[dt][jj] * inv;
-      }
-      *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * g) = ov;
-      if (vrow) *reinterpret_cast<f32x4*>(vrow + 16 * dt + 4 * g) = vv;
+      *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * g) = ov[dt];
+      if (vrow) *reinterpret_cast<f32x4*>(vrow + 16 * dt + 4 * g) = vv[dt];
     }
     if (g == 0) {
       if (lse) lse[(size_t)bh * T + my_q] = (m_run + __log2f(e_tot)) * kLn2;
       if (c_aux) c_aux[(size_t)bh * T + my_q] = cc;
+      if (cor) cor[(size_t)bh * T + my_q] = __builtin_sqrtf(n_c) / __builtin_sqrtf(n_o);
     }
   }
 }
 
 template <int D, int NW>
 hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void* rho, float* o,
-                        float* lse, float* c_aux, float* vbar_aux, int B, int Hq, int Hkv, int T,
-                        float scale, hipStream_t stream) {
+                        float* lse, float* c_aux, float* vbar_aux, float* cor, unsigned flags, int B,
+                        int Hq, int Hkv, int T, float scale, hipStream_t stream) {
   const int nqb = (T + 16 * NW - 1) / (16 * NW);
   hipLaunchKernelGGL((fwd16_kernel<D, NW>), dim3(nqb * B * Hq), dim3(64 * NW), 0, stream,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)rho, o,
-                     lse, c_aux, vbar_aux, B, Hq, Hkv, T, scale * kLog2e);
+                     lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale * kLog2e);
   return hipGetLastError();
 }
 
 template <class Pol, int D>
 hipError_t launch_fwd_t(const void* q, const void* k, const void* v, const void* rho, float* o,
-                        float* lse, float* c_aux, float* vbar_aux, int B, int Hq, int Hkv, int T,
-                        float scale, hipStream_t stream) {
+                        float* lse, float* c_aux, float* vbar_aux, float* cor, unsigned flags, int B,
+                        int Hq, int Hkv, int T, float scale, hipStream_t stream) {
   using in_t = typename Pol::in_t;
   const int nqb = (T + FWD_BR - 1) / FWD_BR;
   dim3 grid(nqb * B * Hq);
   hipLaunchKernelGGL((fwd_kernel<Pol, D>), grid, dim3(FWD_THREADS), 0, stream,
                      (const in_t*)q, (const in_t*)k, (const in_t*)v, (const in_t*)rho, o, lse, c_aux,
-                     vbar_aux, B, Hq, Hkv, T, scale * kLog2e);
+                     vbar_aux, cor, flags, B, Hq, Hkv, T, scale * kLog2e);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd(int dtype, const void* q, const void* k, const void* v, const void* rho,
-                      float* o, float* lse, float* c_aux, float* vbar_aux, int B, int Hq, int Hkv,
-                      int T, int d, float scale, hipStream_t stream) {
+                      float* o, float* lse, float* c_aux, float* vbar_aux, float* cor,
+                      unsigned flags, int B, int Hq, int Hkv, int T, int d, float scale,
+                      hipStream_t stream) {
   if (dtype == PLX_BF16) {
-    if (d == 64) return launch_fwd16<64, FWD16_WAVES>(q, k, v, rho, o, lse, c_aux, vbar_aux, B, Hq, Hkv, T, scale, stream);
-    return launch_fwd16<128, FWD16_WAVES>(q, k, v, rho, o, lse, c_aux, vbar_aux, B, Hq, Hkv, T, scale, stream);
+    if (d == 64)
+      return launch_fwd16<64, FWD16_WAVES>(q, k, v, rho, o, lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale, stream);
+    return launch_fwd16<128, FWD16_WAVES>(q, k, v, rho, o, lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale, stream);
   }
-  if (d == 64) return launch_fwd_t<PolF32, 64>(q, k, v, rho, o, lse, c_aux, vbar_aux, B, Hq, Hkv, T, scale, stream);
-  return launch_fwd_t<PolF32, 128>(q, k, v, rho, o, lse, c_aux, vbar_aux, B, Hq, Hkv, T, scale, stream);
+  if (d == 64)
+    return launch_fwd_t<PolF32, 64>(q, k, v, rho, o, lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale, stream);
+  return launch_fwd_t<PolF32, 128>(q, k, v, rho, o, lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale, stream);
 }
 
 }  // namespace plx

@@ -10,9 +10,11 @@
 
 namespace plx {
 
+// flags: PLX_UNIFORM_WEIGHTS | PLX_NO_INTERCEPT; cor may be NULL.
 hipError_t launch_fwd(int dtype, const void* q, const void* k, const void* v, const void* rho,
-                      float* o, float* lse, float* c_aux, float* vbar_aux, int B, int Hq, int Hkv,
-                      int T, int d, float scale, hipStream_t stream);
+                      float* o, float* lse, float* c_aux, float* vbar_aux, float* cor,
+                      unsigned flags, int B, int Hq, int Hkv, int T, int d, float scale,
+                      hipStream_t stream);
 
 // Decode: key-split partial kernel followed by the merge kernel.
 int decode_auto_splits(int B, int Hkv, int S_max);
@@ -21,9 +23,9 @@ size_t decode_record_floats(int d);
 int decode_balanced_ctas(int B, int Hkv, int S_max);
 size_t decode_balanced_records(int B, int Hq, int Hkv, int S_max);
 hipError_t launch_decode(int dtype, const void* q, const void* rho, const void* k_cache,
-                         const void* v_cache, const int32_t* ctx_len, float* o, float* lse, int B,
-                         int Hq, int Hkv, int S_max, int d, float scale, int num_splits,
-                         float* partials, hipStream_t stream);
+                         const void* v_cache, const int32_t* ctx_len, float* o, float* lse,
+                         float* cor, unsigned flags, int B, int Hq, int Hkv, int S_max, int d,
+                         float scale, int num_splits, float* partials, hipStream_t stream);
 
 // Backward: workspace bytes (G and delta, then the fp16 input copies of the bf16 path).
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int d);

@@ -134,3 +134,48 @@ def test_bwd_workspace_size():
     head = (2 * B * Hq * T * 4 + 255) // 256 * 256
     assert binding.bwd_workspace_size(B, Hq, Hkv, T, d) == head + (3 * B * Hq * T * d + 2 * B * Hkv * T * d) * 2
     assert binding.bwd_workspace_size(8, 16, 8, 0, 128) == 0
+
+
+def _fwd_ex(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, rho=FAKE, o=FAKE, lse=None, c=None, vb=None, cor=None,
+                B=1, Hq=2, Hkv=1, T=16, d=64, scale=0.125, flags=0, dtype=binding.PLX_BF16)
+    args.update(kw)
+    return binding.lib().plx_fwd_prefill_ex(
+        args["q"], args["k"], args["v"], args["rho"], args["o"], args["lse"], args["c"], args["vb"],
+        args["cor"], args["B"], args["Hq"], args["Hkv"], args["T"], args["d"], args["scale"],
+        args["flags"], args["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=4), binding.PLX_ERR_INVALID_ARG),
+    (dict(flags=0xFFFFFFFF), binding.PLX_ERR_INVALID_ARG),
+    (dict(cor=ctypes.c_void_p(0x10002)), binding.PLX_ERR_INVALID_ARG),
+    (dict(lse=ctypes.c_void_p(0x10001)), binding.PLX_ERR_INVALID_ARG),
+    (dict(q=None, flags=3), binding.PLX_ERR_INVALID_ARG),
+    (dict(d=96, flags=1), binding.PLX_ERR_UNSUPPORTED),
+    (dict(T=0, flags=2), binding.PLX_ERR_INVALID_ARG),
+])
+def test_prefill_ex_validation(kw, status):
+    assert _fwd_ex(**kw) == status
+
+
+def _dec_ex(**kw):
+    args = dict(q=FAKE, rho=FAKE, k=FAKE, v=FAKE, ctx=FAKE, o=FAKE, lse=None, cor=None, B=2, Hq=4,
+                Hkv=2, S=1024, d=128, scale=0.1, ns=0, flags=0, ws=FAKE, ws_bytes=1 << 30,
+                dtype=binding.PLX_BF16)
+    args.update(kw)
+    return binding.lib().plx_decode_ex(
+        args["q"], args["rho"], args["k"], args["v"], args["ctx"], args["o"], args["lse"],
+        args["cor"], args["B"], args["Hq"], args["Hkv"], args["S"], args["d"], args["scale"],
+        args["ns"], args["flags"], args["ws"], args["ws_bytes"], args["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=8), binding.PLX_ERR_INVALID_ARG),
+    (dict(cor=ctypes.c_void_p(0x10003)), binding.PLX_ERR_INVALID_ARG),
+    (dict(ctx=ctypes.c_void_p(0x10002)), binding.PLX_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=2, flags=1), binding.PLX_ERR_UNSUPPORTED),
+    (dict(ws_bytes=16, flags=3), binding.PLX_ERR_WORKSPACE),
+])
+def test_decode_ex_validation(kw, status):
+    assert _dec_ex(**kw) == status
