@@ -45,6 +45,13 @@ section "Risultati Sperimentali", and the metric of "Внимание новог
 поколения...", section "Анализ Parallax: Выводы из внутренних метрик") is read
 as ||Sigma_KV rho||_2 / ||o||_2 per query, Euclidean norms over d_v.
 
+Projection (``project_qkvr``): the probe is a learned linear map of the
+layer input, rho_i = W_R x_i ("当注意力学会追问...", section 1.3; technical
+summary, section "Meccanismo Principale"), an extra projection beside the
+query, key and value ones.  Read here as one stacked weight
+[W_Q; W_K; W_V; W_R] applied to every token, each block split into heads of
+d rows, head-major, and the results laid out [B, H, T, d].
+
 All arithmetic is float64 on the exact (already dtype-rounded) inputs.  The
 per-row functions only use +, -, *, @ and sums once the weights are known, so
 ``row_from_weights`` also runs on numpy object arrays of ``fractions.Fraction``
@@ -70,6 +77,7 @@ __all__ = [
     "correction_to_output",
     "prefill_forward_family",
     "decode_forward_family",
+    "project_qkvr",
 ]
 
 
@@ -331,3 +339,23 @@ def decode_forward_family(q, rho, k_cache, v_cache, ctx_len, scale, uniform=Fals
                 q[b, h], k_cache[b, hk, :n], v_cache[b, hk, :n], rho[b, h], scale, uniform,
                 intercept)
     return {"o": o, "lse": lse, "cor": cor}
+
+
+# -- the projection in front of the operator -----------------------------------
+
+
+def project_qkvr(x, W, Hq, Hkv, d):
+    """x: [B, T, D_model]; W: [(2 Hq + 2 Hkv) d, D_model], the row blocks
+    W_Q (Hq d rows), W_K (Hkv d), W_V (Hkv d), W_R (Hq d), head-major inside a
+    block.  Every token's projection is y = W x_t; block rows h d .. h d + d-1
+    are head h.  Returns (q, k, v, rho) shaped [B, H, T, d]."""
+    B, T, _ = x.shape
+    y = x @ W.T  # [B, T, N]
+    outs = []
+    off = 0
+    for H in (Hq, Hkv, Hkv, Hq):
+        blk = y[:, :, off: off + H * d].reshape(B, T, H, d)
+        outs.append(np.ascontiguousarray(blk.transpose(0, 2, 1, 3)))
+        off += H * d
+    assert off == W.shape[0]
+    return tuple(outs)

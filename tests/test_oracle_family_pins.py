@@ -1,7 +1,8 @@
-"""Pins of the oracle's family corners and correction-to-output ratio against
-facts that do not come from the oracle's own code: numpy's covariance, the
-recurrent (state-space) form of causal linear attention, torch's softmax and
-SDPA, exact rational arithmetic, and invariants of the definitions.
+"""Pins of the oracle's family corners, correction-to-output ratio and stacked
+projection against facts that do not come from the oracle's own code: numpy's
+covariance, the recurrent (state-space) form of causal linear attention,
+torch's softmax and SDPA, exact rational and integer arithmetic, one-hot
+placement probes, and invariants of the definitions.
 """
 
 from fractions import Fraction
@@ -178,3 +179,45 @@ def test_decode_family_equals_last_prefill_row(uniform, intercept):
         np.testing.assert_allclose(dec["o"][b], pre["o"][b, :, i], rtol=0, atol=1e-14)
         np.testing.assert_allclose(dec["lse"][b], pre["lse"][b, :, i], rtol=0, atol=1e-14)
         np.testing.assert_allclose(dec["cor"][b], pre["cor"][b, :, i], rtol=1e-14, atol=0)
+
+
+# -- the stacked projection [W_Q; W_K; W_V; W_R] x ------------------------------
+
+def test_projection_exact_integers_brute_force():
+    """Small integers: every output element equals the integer dot product of
+    its weight row and token, computed with Python ints."""
+    g = _rng(20)
+    B, T, D, Hq, Hkv, d = 2, 3, 5, 2, 1, 3
+    x = g.integers(-4, 5, (B, T, D))
+    W = g.integers(-4, 5, ((2 * Hq + 2 * Hkv) * d, D))
+    q, k, v, rho = orc.project_qkvr(x.astype(np.float64), W.astype(np.float64), Hq, Hkv, d)
+    blocks = [(q, Hq, 0), (k, Hkv, Hq * d), (v, Hkv, (Hq + Hkv) * d), (rho, Hq, (Hq + 2 * Hkv) * d)]
+    for out, H, base in blocks:
+        assert out.shape == (B, H, T, d)
+        for b in range(B):
+            for h in range(H):
+                for t in range(T):
+                    for j in range(d):
+                        row = W[base + h * d + j]
+                        assert out[b, h, t, j] == sum(int(row[c]) * int(x[b, t, c]) for c in range(D))
+
+
+def test_projection_one_hot_tokens_place_weight_columns():
+    """x_t = e_c(t) picks weight column c(t), so out[b,h,t,:] is the slice of
+    that column belonging to (block, head): a placement probe for the layout."""
+    B, T, Hq, Hkv, d = 2, 5, 4, 2, 4
+    N = (2 * Hq + 2 * Hkv) * d
+    D = B * T
+    W = np.arange(N * D, dtype=np.float64).reshape(N, D)
+    x = np.zeros((B, T, D))
+    for b in range(B):
+        for t in range(T):
+            x[b, t, b * T + t] = 1.0
+    q, k, v, rho = orc.project_qkvr(x, W, Hq, Hkv, d)
+    for b in range(B):
+        for t in range(T):
+            col = W[:, b * T + t]
+            np.testing.assert_array_equal(q[b, :, t].reshape(-1), col[: Hq * d])
+            np.testing.assert_array_equal(k[b, :, t].reshape(-1), col[Hq * d: (Hq + Hkv) * d])
+            np.testing.assert_array_equal(v[b, :, t].reshape(-1), col[(Hq + Hkv) * d: (Hq + 2 * Hkv) * d])
+            np.testing.assert_array_equal(rho[b, :, t].reshape(-1), col[(Hq + 2 * Hkv) * d:])

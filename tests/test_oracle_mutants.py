@@ -195,3 +195,45 @@ def test_unmutated_oracle_passes_every_family_pin():
         fn(*args)
         n += 1
     assert n >= 12
+
+
+_project = orc.project_qkvr
+
+
+def _pm_kv_swapped(x, W, Hq, Hkv, d):
+    q, k, v, rho = _project(x, W, Hq, Hkv, d)
+    return q, v, k, rho
+
+
+def _pm_dim_major(x, W, Hq, Hkv, d):
+    B, T, _ = x.shape
+    y = x @ W.T
+    outs, off = [], 0
+    for H in (Hq, Hkv, Hkv, Hq):
+        blk = y[:, :, off: off + H * d].reshape(B, T, d, H).transpose(0, 3, 1, 2)
+        outs.append(np.ascontiguousarray(blk))
+        off += H * d
+    return tuple(outs)
+
+
+def _pm_dim_reversed(x, W, Hq, Hkv, d):
+    return tuple(np.ascontiguousarray(t[..., ::-1]) for t in _project(x, W, Hq, Hkv, d))
+
+
+def _pm_heads_of_block_swapped(x, W, Hq, Hkv, d):
+    q, k, v, rho = _project(x, W, Hq, Hkv, d)
+    return q[:, ::-1].copy(), k, v, rho
+
+
+@pytest.mark.parametrize("mutant", [_pm_kv_swapped, _pm_dim_major, _pm_dim_reversed, _pm_heads_of_block_swapped],
+                         ids=lambda f: f.__name__)
+def test_projection_pins_catch_mutant(mutant, monkeypatch):
+    monkeypatch.setattr(orc, "project_qkvr", mutant)
+    caught = []
+    for fn in (fpins.test_projection_exact_integers_brute_force,
+               fpins.test_projection_one_hot_tokens_place_weight_columns):
+        try:
+            fn()
+        except Exception:
+            caught.append(fn.__name__)
+    assert caught, f"no pin caught {mutant.__name__}"
