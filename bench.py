@@ -240,6 +240,45 @@ def bench_train(steps, warmup):
     return out
 
 
+# --------------------------------------------------------------- projection
+def bench_proj(steps, warmup):
+    """The stacked [W_Q; W_K; W_V; W_R] projection of the prefill workload's
+    layer (B=4, T=4096, D=1024 -> Hq=16, Hkv=8, d=128).  torch.matmul of the
+    same shapes (a library GEMM writing one [B T, N] matrix, no head-major
+    scatter) is timed beside it for context."""
+    import torch
+
+    from parallax_local_linear_plx_amd import inputs, plx_qkvr_proj
+
+    B, T, D, Hq, Hkv, d = 4, 4096, 1024, 16, 8, 128
+    N = (2 * Hq + 2 * Hkv) * d
+    x = inputs.device_normal((B, T, D), 1.0, 61)
+    w = inputs.device_normal((N, D), 1.0 / np.sqrt(D), 62)
+    out = plx_qkvr_proj(x, w, Hq, Hkv, d)
+
+    def step():
+        plx_qkvr_proj(x, w, Hq, Hkv, d, out=out)
+
+    ms = time_steps(step, steps, warmup)
+    x2, wt = x.view(B * T, D), w.t()
+    y = torch.empty((B * T, N), dtype=torch.bfloat16, device="cuda")
+    ms_lib = time_steps(lambda: torch.matmul(x2, wt, out=y), steps, warmup)
+    flops = 2 * B * T * N * D
+    algo_bytes = (B * T * D + N * D + B * T * N) * 2
+    tf = flops / (ms * 1e-3) / 1e12
+    del x, w, out, y
+    torch.cuda.empty_cache()
+    return {"workload": f"bf16 stacked projection [Q|K|V|rho] = x W^T, B={B} T={T} D={D} "
+                        f"Hq={Hq} Hkv={Hkv} d={d} (N={N}), head-major outputs",
+            "us_per_call": ms * 1e3, "tflops": tf, "flops": flops, "bytes": algo_bytes,
+            "library_matmul_us": ms_lib * 1e3,
+            "library_matmul_tflops": flops / (ms_lib * 1e-3) / 1e12,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic("proj"), "kernel": "proj_kernel",
+                         "algorithmic_flops_per_launch": flops}}
+
+
 # -------------------------------------------------------- copy calibration
 def bench_copy(steps, nbytes=1 << 30):
     """A plain device-to-device copy of a known size.  Run under rocprofv3
@@ -259,6 +298,7 @@ TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "prefill": ["plx_fwd.hip", "plx_common.hpp"],
     "decode": ["plx_decode.hip", "plx_common.hpp"],
+    "proj": ["plx_proj.hip", "plx_common.hpp"],
 }
 
 
@@ -335,7 +375,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--only", default="all",
-                    choices=["all", "prefill", "decode", "decode_long", "train", "copy", "decode_sweep"])
+                    choices=["all", "prefill", "decode", "decode_long", "train", "proj", "copy",
+                             "decode_sweep"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay decode timing")
     args = ap.parse_args()
@@ -383,6 +424,11 @@ def main():
                                           "bf16 long-context decode B=8 Hq=16 Hkv=8 "
                                           "ctx~U{16384..131072} d=128, split-K", 41, not args.no_graph)
         log(f"  {res['decode_long']['us_per_step']:.1f} us  {res['decode_long']['GB/s']:.0f} GB/s")
+    if args.only in ("all", "proj"):
+        log("stacked projection ...")
+        res["proj"] = bench_proj(args.steps, args.warmup)
+        log(f"  {res['proj']['us_per_call']:.1f} us  {res['proj']['tflops']:.1f} TFLOP/s "
+            f"(library matmul {res['proj']['library_matmul_us']:.1f} us)")
     if args.only in ("all", "train"):
         log("training step ...")
         res["train"] = bench_train(max(3, args.steps // 4), max(1, args.warmup // 2))
@@ -403,7 +449,7 @@ def main():
                                   "algorithmic_flops_per_launch": p["flops"]}})
     else:
         line.update({"value": None, "unit": "TFLOP/s", "ms_per_step": None, "config": {"workload": args.only}})
-    for key in ("decode", "decode_long", "train"):
+    for key in ("decode", "decode_long", "train", "proj"):
         if key in res:
             line[key] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res[key].items()}
             if key.startswith("decode"):

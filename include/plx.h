@@ -184,6 +184,32 @@ plx_status plx_decode_ex(const void* q, const void* rho, const void* k_cache, co
                          plx_stream stream);
 
 /*
+ * The projection in front of the operator.
+ *
+ * The probe is a learned linear map of the layer input, rho_i = W_R x_i
+ * ("当注意力学会追问..." (zhichai.net), section 1.3; "Riepilogo Tecnico:
+ * Parallax ...", section "Meccanismo Principale").  With the query, key and
+ * value projections it forms one GEMM over the stacked weight
+ * W = [W_Q; W_K; W_V; W_R]: for every token, y = W x_t, and the four row
+ * blocks of y, split into heads of d rows, are written in the [B, H, T, d]
+ * layout the other entry points read.
+ *
+ *   x      [B, T, D] bf16 (the layer input, tokens of one sequence consecutive)
+ *   w      [(2 Hq + 2 Hkv) d, D] bf16: rows [0, Hq d) W_Q, then Hkv d rows of
+ *          W_K, Hkv d rows of W_V and Hq d rows of W_R; inside a block, row
+ *          h d + j is dimension j of head h
+ *   q, rho [B, Hq, T, d] bf16, written;  k, v [B, Hkv, T, d] bf16, written
+ * Products accumulate in fp32 and each output is rounded to bf16 (to nearest,
+ * ties to even).  Requires dtype = PLX_BF16 (else PLX_ERR_UNSUPPORTED),
+ * D % 64 == 0 (else PLX_ERR_UNSUPPORTED), d in {64, 128}, B, T, Hq, Hkv >= 1,
+ * Hq % Hkv == 0 and 16-byte aligned pointers.  The outputs must not overlap
+ * x or w.
+ */
+plx_status plx_qkvr_proj(const void* x, const void* w, void* q, void* k, void* v, void* rho,
+                         int B, int T, int D, int Hq, int Hkv, int d, plx_dtype dtype,
+                         plx_stream stream);
+
+/*
  * Backward of the causal prefill (the pages give none; these are the exact
  * gradients of the forward above with rho an independent input).
  *

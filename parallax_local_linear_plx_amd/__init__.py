@@ -16,5 +16,6 @@ from .binding import (  # noqa: F401
     plx_decode_ex,
     plx_fwd_prefill,
     plx_fwd_prefill_ex,
+    plx_qkvr_proj,
     status_string,
 )

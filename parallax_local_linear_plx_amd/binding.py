@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.plx_decode.restype = _i
     L.plx_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _vp]
+    L.plx_qkvr_proj.restype = _i
+    L.plx_qkvr_proj.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]
     L.plx_bwd_workspace_size.restype = _sz
     L.plx_bwd_workspace_size.argtypes = [_i, _i, _i, _i, _i]
     L.plx_bwd.restype = _i
@@ -229,6 +231,30 @@ def _decode(q, rho, k_cache, v_cache, ctx_len, scale, *, num_splits, workspace, 
             out["cor"] = cor_t
     if lse_t is not None:
         out["lse"] = lse_t
+    return out
+
+
+def plx_qkvr_proj(x, w, Hq, Hkv, d, *, out=None):
+    """Stacked projection.  x [B,T,D] bf16; w [(2Hq+2Hkv)d, D] bf16 (rows W_Q,
+    W_K, W_V, W_R).  Returns dict(q, k, v, rho) in the [B,H,T,d] layout (bf16)."""
+    torch = _torch()
+    B, T, D = x.shape
+    dev = x.device
+    N = (2 * Hq + 2 * Hkv) * d
+    _need(w, "w", (N, D), x.dtype, dev)
+    if out is None:
+        out = {
+            "q": torch.empty((B, Hq, T, d), dtype=x.dtype, device=dev),
+            "k": torch.empty((B, Hkv, T, d), dtype=x.dtype, device=dev),
+            "v": torch.empty((B, Hkv, T, d), dtype=x.dtype, device=dev),
+            "rho": torch.empty((B, Hq, T, d), dtype=x.dtype, device=dev),
+        }
+    for n, H in (("q", Hq), ("k", Hkv), ("v", Hkv), ("rho", Hq)):
+        _need(out[n], n, (B, H, T, d), x.dtype, dev)
+    _need(x, "x", (B, T, D), x.dtype, dev)
+    st = lib().plx_qkvr_proj(_ptr(x), _ptr(w), _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]),
+                             _ptr(out["rho"]), B, T, D, Hq, Hkv, d, _dtype_code(x), _stream(dev))
+    _check(st, "plx_qkvr_proj")
     return out
 
 

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libplx.so")
 
-SOURCES = ["plx_api.cpp", "plx_fwd.hip", "plx_decode.hip", "plx_bwd.hip"]
+SOURCES = ["plx_api.cpp", "plx_fwd.hip", "plx_decode.hip", "plx_bwd.hip", "plx_proj.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -148,4 +148,20 @@ plx_status plx_bwd(const void* q, const void* k, const void* v, const void* rho,
                                   (hipStream_t)stream));
 }
 
+plx_status plx_qkvr_proj(const void* x, const void* w, void* q, void* k, void* v, void* rho, int B,
+                         int T, int D, int Hq, int Hkv, int d, plx_dtype dtype, plx_stream stream) {
+  if (!x || !w || !q || !k || !v || !rho) return PLX_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype) || T < 1 || D < 1) return PLX_ERR_INVALID_ARG;
+  plx_status st = check_heads(B, Hq, Hkv, d);
+  if (st != PLX_OK) return st;
+  if (dtype != PLX_BF16 || D % 64 != 0) return PLX_ERR_UNSUPPORTED;
+  const long long M = (long long)B * T, N = (2LL * Hq + 2LL * Hkv) * d;
+  if (M * D >= (1LL << 40) || N * D >= (1LL << 40) || M * N >= (1LL << 40) || M >= (1LL << 31))
+    return PLX_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, w, q, k, v, rho};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return PLX_ERR_INVALID_ARG;
+  return from_hip(plx::launch_proj(x, w, q, k, v, rho, B, T, D, Hq, Hkv, d, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -34,4 +34,8 @@ hipError_t launch_bwd(int dtype, const void* q, const void* k, const void* v, co
                       const float* vbar_aux, float* dq, float* dk, float* dv, float* drho, int B,
                       int Hq, int Hkv, int T, int d, float scale, float* ws, hipStream_t stream);
 
+// Stacked projection [Q | K | V | rho] = X W^T into the [B, H, T, d] layout.
+hipError_t launch_proj(const void* x, const void* w, void* q, void* k, void* v, void* rho, int B,
+                       int T, int D, int Hq, int Hkv, int d, hipStream_t stream);
+
 }  // namespace plx

@@ -1,0 +1,203 @@
+// The projection in front of the operator: one GEMM that forms the query,
+// key, value and probe of every token, written straight into the head-major
+// [B, H, T, d] layout the attention kernels read.
+//
+// The probe is a learned linear map of the layer input, rho_i = W_R x_i
+// ("当注意力学会追问...", section 1.3; "Riepilogo Tecnico: Parallax ...",
+// section "Meccanismo Principale"), a fourth projection beside W_Q, W_K and
+// W_V.  Stacking the four weights as W = [W_Q; W_K; W_V; W_R] (N = (2 Hq +
+// 2 Hkv) d rows, D columns) turns them into one GEMM  Y = X W^T  over the
+// M = B T tokens, so the layer input is read once for all four.
+//
+// Kernel: 256 x 256 output tiles (tokens x features), eight waves, two per
+// SIMD, each owning 128 features x 64 tokens of the tile as 4 x 2 accumulators
+// of the 32x32x16 bf16 MFMA (fp32).  64-deep W and X tiles are
+// double-buffered in LDS; the global loads of tile t+1 are issued at the start
+// of tile t and stored at its end.  The operands of each 16-deep step are read
+// from LDS while the previous step's MFMAs run; at a tile boundary the barrier
+// and the first reads of the next tile sit before the last step's MFMAs.  The
+// epilogue rounds to bf16 (round to nearest even), transposes each wave's tile
+// through LDS and stores whole rows of d, one head per 16-lane group.
+#include "plx_common.hpp"
+#include "plx_kernels.hpp"
+
+namespace plx {
+
+namespace {
+
+constexpr int PJ_BM = 256;      // tokens per workgroup
+constexpr int PJ_BN = 256;      // output features per workgroup
+constexpr int PJ_BK = 64;       // reduction depth of one LDS tile
+constexpr int PJ_THREADS = 512;
+constexpr int PJ_LD = PJ_BK + 8;  // LDS row stride (elements): 144 B, conflict-free b128 reads
+constexpr int PJ_OLD = 128 + 8;   // epilogue row stride (elements)
+constexpr int PJ_CH = PJ_BM * PJ_BK / 8 / PJ_THREADS;  // 16-byte chunks per thread per operand tile
+
+struct ProjSmem {
+  union {
+    struct {
+      uint16_t w[2][PJ_BN * PJ_LD];
+      uint16_t x[2][PJ_BM * PJ_LD];
+    } in;
+    uint16_t out[8][64 * PJ_OLD];  // one 64 x 128 bf16 tile per wave
+  };
+};
+
+__device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
+  const __bf16 ha = static_cast<__bf16>(a), hb = static_cast<__bf16>(b);
+  return (unsigned)__builtin_bit_cast(uint16_t, ha) | ((unsigned)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+__global__ __launch_bounds__(PJ_THREADS, 1) void proj_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, uint16_t* __restrict__ q,
+    uint16_t* __restrict__ k, uint16_t* __restrict__ v, uint16_t* __restrict__ rho, int T, int K,
+    int Hq, int Hkv, int d, int M, int N) {
+  __shared__ ProjSmem sm;
+  const int nmb = (M + PJ_BM - 1) / PJ_BM;
+  const int nnb = (N + PJ_BN - 1) / PJ_BN;
+  // tiles of one feature block are consecutive, and consecutive tiles share an
+  // XCD, so the eight that run together on one XCD read the same W tile
+  const int lin = xcd_block_order(blockIdx.x, nmb, nmb * nnb);
+  const int m0 = (lin % nmb) * PJ_BM;
+  const int n0 = (lin / nmb) * PJ_BN;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wave & 1, wm = wave >> 1;  // wave tile: features wn*128.., tokens wm*64..
+  const int l32 = lane & 31, h = lane >> 5;
+
+  // global -> register staging of one 64-deep tile of W and X (rows past the
+  // end read the last row: finite, and their results are never stored)
+  u32x4 sw[PJ_CH], sx[PJ_CH];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < PJ_CH; ++i) {
+      const int it = threadIdx.x + PJ_THREADS * i;
+      const int row = it >> 3, c = (it & 7) * 8;
+      sw[i] = *reinterpret_cast<const u32x4*>(w + (size_t)min(n0 + row, N - 1) * K + k0 + c);
+      sx[i] = *reinterpret_cast<const u32x4*>(x + (size_t)min(m0 + row, M - 1) * K + k0 + c);
+    }
+  };
+  auto lds_put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PJ_CH; ++i) {
+      const int it = threadIdx.x + PJ_THREADS * i;
+      const int row = it >> 3, c = (it & 7) * 8;
+      *reinterpret_cast<u32x4*>(&sm.in.w[buf][row * PJ_LD + c]) = sw[i];
+      *reinterpret_cast<u32x4*>(&sm.in.x[buf][row * PJ_LD + c]) = sx[i];
+    }
+  };
+  // operands of one 16-deep step: A = W rows (features), B = X rows (tokens);
+  // lane (l32, h) supplies row l32 of each 32-row block and depth 8h .. 8h+7
+  struct Ops { bf16x8 a[4], b[2]; };
+  auto read_ops = [&](Ops& o, int buf, int ks) {
+    const uint16_t* wr = &sm.in.w[buf][(wn * 128 + l32) * PJ_LD + 16 * ks + 8 * h];
+    const uint16_t* xr = &sm.in.x[buf][(wm * 64 + l32) * PJ_LD + 16 * ks + 8 * h];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.a[i] = *reinterpret_cast<const bf16x8*>(wr + 32 * i * PJ_LD);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) o.b[i] = *reinterpret_cast<const bf16x8*>(xr + 32 * i * PJ_LD);
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+  auto mfmas = [&](const Ops& o) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[i], o.b[j], acc[i][j], 0, 0, 0);
+  };
+
+  const int ntiles = K / PJ_BK;
+  gload(0);
+  lds_put(0);
+  __syncthreads();
+  Ops cur, nxt;
+  read_ops(cur, 0, 0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    const bool more = t + 1 < ntiles;
+    if (more) gload((t + 1) * PJ_BK);
+#pragma unroll
+    for (int ks = 0; ks < PJ_BK / 16 - 1; ++ks) {
+      read_ops(nxt, buf, ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(cur);
+      __builtin_amdgcn_sched_barrier(0);
+      cur = nxt;
+    }
+    // last step of the tile: stage tile t+1 into the other buffer (its tile
+    // t-1 was read before the previous barrier), make it visible, start
+    // reading its first step, then issue this step's MFMAs
+    if (more) lds_put(buf ^ 1);
+    __syncthreads();
+    if (more) read_ops(nxt, buf ^ 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(cur);
+    __builtin_amdgcn_sched_barrier(0);
+    cur = nxt;
+  }
+  __syncthreads();  // every wave is done with the operand buffers
+
+  // epilogue: acc[i][j][r] is feature wn*128 + 32 i + 8 (r/4) + 4 h + r%4 and
+  // token wm*64 + 32 j + l32; round to bf16 and transpose through LDS
+  uint16_t* ot = sm.out[wave];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int nl = 32 * i + 8 * g + 4 * h, ml = 32 * j + l32;
+        uint2 pk;
+        pk.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+        pk.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        *reinterpret_cast<uint2*>(&ot[ml * PJ_OLD + nl]) = pk;
+      }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // 16 lanes per token row, 8 features each: a head's whole d-row per group
+  const int nq = Hq * d, nk = nq + Hkv * d, nv = nk + Hkv * d;
+#pragma unroll 4
+  for (int i = 0; i < 64 * 16 / 64; ++i) {
+    const int it = 64 * i + lane;
+    const int row = it >> 4, c = (it & 15) * 8;
+    const int m = m0 + wm * 64 + row, n = n0 + wn * 128 + c;
+    if (m >= M || n >= N) continue;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(&ot[row * PJ_OLD + c]);
+    uint16_t* base;
+    int H, loc;
+    if (n < nq) {
+      base = q, H = Hq, loc = n;
+    } else if (n < nk) {
+      base = k, H = Hkv, loc = n - nq;
+    } else if (n < nv) {
+      base = v, H = Hkv, loc = n - nk;
+    } else {
+      base = rho, H = Hq, loc = n - nv;
+    }
+    const int b = m / T, tt = m - b * T;
+    const int head = loc / d, dd = loc - head * d;
+    *reinterpret_cast<u32x4*>(base + (((size_t)b * H + head) * T + tt) * d + dd) = val;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_proj(const void* x, const void* w, void* q, void* k, void* v, void* rho, int B,
+                       int T, int D, int Hq, int Hkv, int d, hipStream_t stream) {
+  const int M = B * T, N = (2 * Hq + 2 * Hkv) * d;
+  const int tiles = ((M + PJ_BM - 1) / PJ_BM) * ((N + PJ_BN - 1) / PJ_BN);
+  hipLaunchKernelGGL(proj_kernel, dim3(tiles), dim3(PJ_THREADS), 0, stream, (const uint16_t*)x,
+                     (const uint16_t*)w, (uint16_t*)q, (uint16_t*)k, (uint16_t*)v, (uint16_t*)rho, T, D,
+                     Hq, Hkv, d, M, N);
+  return hipGetLastError();
+}
+
+}  // namespace plx

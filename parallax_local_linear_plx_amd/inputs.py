@@ -7,7 +7,8 @@ HIP path and the fp64 CPU oracle can consume what it produces.
 Draw recipe (one ``numpy.random.SeedSequence(seed)`` per workload):
 
 * the root sequence is spawned into fixed roles, in this order:
-  ``ctx_len, q, k, v, rho (or x), w_r, d_o``;
+  ``ctx_len, q, k, v, rho (or x), w_r, d_o, x_in, w_qkvr`` (the last two for
+  the stacked projection in front of the operator);
 * every large tensor is drawn per leading ``(b, h)`` slice from a further
   ``spawn`` of its role, so any slice can be regenerated on its own and the
   slices can be filled by threads in parallel;
@@ -29,7 +30,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # Fixed role order inside one workload's SeedSequence.
-_ROLES = ("ctx_len", "q", "k", "v", "rho", "w_r", "d_o")
+_ROLES = ("ctx_len", "q", "k", "v", "rho", "w_r", "d_o", "x_in", "w_qkvr")
 
 
 def _threads() -> int:
@@ -154,6 +155,19 @@ def make_prefill(B, Hq, Hkv, T, d, dtype="bf16", seed=0, rho_std=0.1,
         wl.tensors["rho"] = _fill_normal(r["rho"], (B, Hq, T, d), rho_std, dtype)
     if with_grad:
         wl.tensors["d_o"] = _fill_normal(r["d_o"], (B, Hq, T, d), 1.0, dtype)
+    return wl
+
+
+def make_projection(B, T, D, Hq, Hkv, d, dtype="bf16", seed=0, name="projection") -> Workload:
+    """Layer input x [B, T, D] ~ N(0, 1) and the stacked weight
+    [W_Q; W_K; W_V; W_R] [(2 Hq + 2 Hkv) d, D] ~ N(0, 1/D), so every projected
+    component is ~ N(0, 1) like the operator's q, k, v and projected rho."""
+    r = _roles(seed)
+    N = (2 * Hq + 2 * Hkv) * d
+    wl = Workload(name, dtype, B, Hq, Hkv, d, 1.0 / np.sqrt(d), T=T)
+    wl.tensors["x"] = _fill_normal(r["x_in"], (B, T, D), 1.0, dtype)
+    w = _fill_normal(r["w_qkvr"], (1, N, D), 1.0 / np.sqrt(D), dtype)
+    wl.tensors["w"] = Tensor(w.dtype, w.data.reshape(N, D))
     return wl
 
 

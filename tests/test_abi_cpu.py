@@ -179,3 +179,28 @@ def _dec_ex(**kw):
 ])
 def test_decode_ex_validation(kw, status):
     assert _dec_ex(**kw) == status
+
+
+def _proj(**kw):
+    args = dict(x=FAKE, w=FAKE, q=FAKE, k=FAKE, v=FAKE, r=FAKE, B=1, T=16, D=128, Hq=2, Hkv=1, d=64,
+                dtype=binding.PLX_BF16)
+    args.update(kw)
+    return binding.lib().plx_qkvr_proj(args["x"], args["w"], args["q"], args["k"], args["v"], args["r"],
+                                       args["B"], args["T"], args["D"], args["Hq"], args["Hkv"],
+                                       args["d"], args["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), binding.PLX_ERR_INVALID_ARG),
+    (dict(r=None), binding.PLX_ERR_INVALID_ARG),
+    (dict(T=0), binding.PLX_ERR_INVALID_ARG),
+    (dict(D=0), binding.PLX_ERR_INVALID_ARG),
+    (dict(D=96), binding.PLX_ERR_UNSUPPORTED),
+    (dict(d=32), binding.PLX_ERR_UNSUPPORTED),
+    (dict(Hq=3, Hkv=2), binding.PLX_ERR_INVALID_ARG),
+    (dict(dtype=binding.PLX_F32), binding.PLX_ERR_UNSUPPORTED),
+    (dict(dtype=9), binding.PLX_ERR_INVALID_ARG),
+    (dict(w=ctypes.c_void_p(0x10008)), binding.PLX_ERR_INVALID_ARG),
+])
+def test_proj_validation(kw, status):
+    assert _proj(**kw) == status
