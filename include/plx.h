@@ -32,7 +32,9 @@
  *     well in plx_bwd) must lie within fp16's range, |x| <= 65504: the
  *     conversion is exact down to 2^-14 and rounds smaller magnitudes to fp16's
  *     subnormal grid (absolute error <= 2^-25); larger ones become infinite.
- *   - Supported head dims: d = 64 or 128 (d_k = d_v = d).
+ *   - Supported head dims: d = 64 or 128 (d_k = d_v = d) everywhere; d = 256 as
+ *     well for bf16 in plx_fwd_prefill(_ex), plx_decode(_ex) and plx_qkvr_proj
+ *     (PLX_ERR_UNSUPPORTED for fp32 and for plx_bwd).
  *   - All pointers are DEVICE pointers unless stated.  The caller owns every
  *     buffer; the library never allocates or frees device memory and keeps no
  *     state between calls.  Calls are asynchronous on `stream` (a hipStream_t;
@@ -91,7 +93,7 @@ const char* plx_status_string(plx_status s);
  *   vbar_aux    [B, Hq, T, d]   fp32 vbar_i (the softmax-attention output), or NULL
  *   scale       tau > 0 (finite)
  * lse, c_aux and vbar_aux are the auxiliaries plx_bwd needs.
- * Requires B, Hq, Hkv, T >= 1, Hq % Hkv == 0, d in {64, 128}, 16-byte aligned
+ * Requires B, Hq, Hkv, T >= 1, Hq % Hkv == 0, d in {64, 128} (or 256, bf16), 16-byte aligned
  * pointers.  A T that is not a multiple of any tile size is handled exactly.
  */
 plx_status plx_fwd_prefill(const void* q, const void* k, const void* v, const void* rho,
@@ -201,7 +203,7 @@ plx_status plx_decode_ex(const void* q, const void* rho, const void* k_cache, co
  *   q, rho [B, Hq, T, d] bf16, written;  k, v [B, Hkv, T, d] bf16, written
  * Products accumulate in fp32 and each output is rounded to bf16 (to nearest,
  * ties to even).  Requires dtype = PLX_BF16 (else PLX_ERR_UNSUPPORTED),
- * D % 64 == 0 (else PLX_ERR_UNSUPPORTED), d in {64, 128}, B, T, Hq, Hkv >= 1,
+ * D % 64 == 0 (else PLX_ERR_UNSUPPORTED), d in {64, 128, 256}, B, T, Hq, Hkv >= 1,
  * Hq % Hkv == 0 and 16-byte aligned pointers.  The outputs must not overlap
  * x or w.
  */

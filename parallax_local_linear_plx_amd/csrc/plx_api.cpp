@@ -16,12 +16,16 @@ bool flags_ok(unsigned f) { return (f & ~(PLX_UNIFORM_WEIGHTS | PLX_NO_INTERCEPT
 
 bool dtype_ok(plx_dtype dt) { return dt == PLX_F32 || dt == PLX_BF16; }
 
-plx_status check_heads(int B, int Hq, int Hkv, int d) {
+// d = 256 is served by the bf16 forward, decode and projection kernels only.
+plx_status check_heads(int B, int Hq, int Hkv, int d, plx_dtype dtype, bool allow256) {
   if (B < 1 || Hq < 1 || Hkv < 1) return PLX_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return PLX_ERR_INVALID_ARG;
+  if (d == 256 && allow256 && dtype == PLX_BF16) return PLX_OK;
   if (d != 64 && d != 128) return PLX_ERR_UNSUPPORTED;
   return PLX_OK;
 }
+
+bool dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 
 bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
@@ -53,7 +57,7 @@ plx_status plx_fwd_prefill_ex(const void* q, const void* k, const void* v, const
                               plx_dtype dtype, plx_stream stream) {
   if (!q || !k || !v || !rho || !o) return PLX_ERR_INVALID_ARG;
   if (!dtype_ok(dtype) || T < 1 || !scale_ok(scale) || !flags_ok(flags)) return PLX_ERR_INVALID_ARG;
-  plx_status st = check_heads(B, Hq, Hkv, d);
+  plx_status st = check_heads(B, Hq, Hkv, d, dtype, true);
   if (st != PLX_OK) return st;
   if (!size_ok((long long)B * Hq * T, d)) return PLX_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rho) || !aligned16(o) ||
@@ -72,7 +76,7 @@ plx_status plx_fwd_prefill(const void* q, const void* k, const void* v, const vo
 
 size_t plx_decode_workspace_size(int B, int Hq, int Hkv, int S_max, int d, int num_splits) {
   if (B < 1 || Hq < 1 || Hkv < 1 || S_max < 1 || num_splits < 0) return 0;
-  if (d != 64 && d != 128) return 0;
+  if (!dim_ok(d)) return 0;
   int ns = num_splits > 0 ? num_splits : plx::decode_auto_splits(B, Hkv, S_max);
   if (ns > S_max) ns = S_max;
   const int chunk = plx::decode_chunk_keys(S_max, ns);
@@ -95,7 +99,7 @@ plx_status plx_decode_ex(const void* q, const void* rho, const void* k_cache, co
   if (!q || !rho || !k_cache || !v_cache || !ctx_len || !o) return PLX_ERR_INVALID_ARG;
   if (!dtype_ok(dtype) || S_max < 1 || num_splits < 0 || !scale_ok(scale) || !flags_ok(flags))
     return PLX_ERR_INVALID_ARG;
-  plx_status st = check_heads(B, Hq, Hkv, d);
+  plx_status st = check_heads(B, Hq, Hkv, d, dtype, true);
   if (st != PLX_OK) return st;
   const int group = Hq / Hkv;
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return PLX_ERR_UNSUPPORTED;
@@ -135,7 +139,7 @@ plx_status plx_bwd(const void* q, const void* k, const void* v, const void* rho,
   if (!q || !k || !v || !rho || !d_o || !o || !lse || !c_aux || !vbar_aux) return PLX_ERR_INVALID_ARG;
   if (!dq || !dk || !dv || !drho) return PLX_ERR_INVALID_ARG;
   if (!dtype_ok(dtype) || T < 1 || !scale_ok(scale)) return PLX_ERR_INVALID_ARG;
-  plx_status st = check_heads(B, Hq, Hkv, d);
+  plx_status st = check_heads(B, Hq, Hkv, d, dtype, false);
   if (st != PLX_OK) return st;
   if (!size_ok((long long)B * Hq * T, d)) return PLX_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, rho, d_o, o, vbar_aux, dq, dk, dv, drho};
@@ -152,7 +156,7 @@ plx_status plx_qkvr_proj(const void* x, const void* w, void* q, void* k, void* v
                          int T, int D, int Hq, int Hkv, int d, plx_dtype dtype, plx_stream stream) {
   if (!x || !w || !q || !k || !v || !rho) return PLX_ERR_INVALID_ARG;
   if (!dtype_ok(dtype) || T < 1 || D < 1) return PLX_ERR_INVALID_ARG;
-  plx_status st = check_heads(B, Hq, Hkv, d);
+  plx_status st = check_heads(B, Hq, Hkv, d, dtype, true);
   if (st != PLX_OK) return st;
   if (dtype != PLX_BF16 || D % 64 != 0) return PLX_ERR_UNSUPPORTED;
   const long long M = (long long)B * T, N = (2LL * Hq + 2LL * Hkv) * d;

@@ -605,7 +605,12 @@ __device__ __forceinline__ void wave_merge(const float* __restrict__ rec0, size_
         const int k = k0 + j;
         ak[j] = k < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), k & 63)) : 0.f;
         const float* r = rec0 + (size_t)min(base + k, n - 1) * stride + 4 + lane * EPL;
-        if constexpr (EPL == 2) {
+        if constexpr (EPL == 4) {
+          const float4 o4 = *reinterpret_cast<const float4*>(r);
+          const float4 u4 = *reinterpret_cast<const float4*>(r + D);
+          ov[j][0] = o4.x, ov[j][1] = o4.y, ov[j][2] = o4.z, ov[j][3] = o4.w;
+          uv[j][0] = u4.x, uv[j][1] = u4.y, uv[j][2] = u4.z, uv[j][3] = u4.w;
+        } else if constexpr (EPL == 2) {
           const float2 o2 = *reinterpret_cast<const float2*>(r);
           const float2 u2 = *reinterpret_cast<const float2*>(r + D);
           ov[j][0] = o2.x, ov[j][1] = o2.y, uv[j][0] = u2.x, uv[j][1] = u2.y;
@@ -915,6 +920,8 @@ hipError_t launch_decode(int dtype, const void* q, const void* rho, const void* 
     const int P = decode_balanced_ctas(B, Hkv, S_max);
     if (d == 64)
       return launch_decode_t<PolBF16, 64>(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, scale, 0, P, partials, stream);
+    if (d == 256)
+      return launch_decode_t<PolBF16, 256>(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, scale, 0, P, partials, stream);
     return launch_decode_t<PolBF16, 128>(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, scale, 0, P, partials, stream);
   }
   int ns = num_splits > 0 ? num_splits : decode_auto_splits(B, Hkv, S_max);
@@ -924,6 +931,8 @@ hipError_t launch_decode(int dtype, const void* q, const void* rho, const void* 
   if (dtype == PLX_BF16) {
     if (d == 64)
       return launch_decode_t<PolBF16, 64>(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, scale, chunk, nsplit, partials, stream);
+    if (d == 256)
+      return launch_decode_t<PolBF16, 256>(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, scale, chunk, nsplit, partials, stream);
     return launch_decode_t<PolBF16, 128>(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, scale, chunk, nsplit, partials, stream);
   }
   if (d == 64)

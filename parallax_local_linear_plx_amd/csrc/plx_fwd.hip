@@ -33,7 +33,16 @@ constexpr int FWD_BR = 128;
 constexpr int FWD_BC = 64;
 constexpr int FWD_THREADS = 256;
 constexpr int FWD16_WAVES = 8;  // waves per workgroup of the bf16 kernel
-constexpr int F16_BC = 128;     // keys per LDS tile of the bf16 kernel
+constexpr int F16_BC = 128;     // keys per LDS tile of the bf16 kernel (d <= 128)
+
+// bf16 kernel shape per head dim: d <= 128 runs 8 waves (two per SIMD) on
+// 128-key tiles; d = 256 runs 4 waves (one per SIMD, whose 512 registers hold
+// the doubled accumulators and operands) on 64-key tiles (LDS holds two
+// double-buffered 64 x 256 K and V tiles).
+template <int D>
+constexpr int f16_bc() { return D > 128 ? 64 : F16_BC; }
+template <int D>
+constexpr int f16_waves() { return D > 128 ? 4 : FWD16_WAVES; }
 // Lazy-rescale threshold (log2 units): p stays <= 16, so the fp16 operand
 // p * r overflows only for |r| = |rho . k| > 4094.
 constexpr float kRescaleLog2 = 4.f;
@@ -498,20 +507,21 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
 // Workgroup: 8 waves, 128 query rows of one (b, h).  Tiles of 128 keys are
 // double-buffered in LDS (K bf16 rows, V fp16 rows); the global loads of tile
 // j+1 are issued at the start of tile j and stored at its end, before the
-// tile's single barrier.
+// tile's single barrier.  At d = 256 the workgroup is 4 waves (64 rows, one
+// wave per SIMD) and the tiles 64 keys (f16_bc, f16_waves).
 template <int D>
 struct Fwd16Smem {
   // row strides (elements), chosen so that the ds_read_b128 of K and the
   // transpose reads of V are free of bank conflicts (measured)
   static constexpr int KLD = D + 16;
   static constexpr int VLD = D + 16;
-  alignas(16) uint16_t k[2][F16_BC * KLD];
-  alignas(16) _Float16 v[2][F16_BC * VLD];
+  alignas(16) uint16_t k[2][f16_bc<D>() * KLD];
+  alignas(16) _Float16 v[2][f16_bc<D>() * VLD];
 };
 
 
 template <int D, int NW>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
+__global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ rho, float* __restrict__ o, float* __restrict__ lse,
     float* __restrict__ c_aux, float* __restrict__ vbar_aux, float* __restrict__ cor,
@@ -521,7 +531,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
   constexpr int NS = D / 32;        // score MFMA steps over d
   constexpr int ND = D / 16;        // 16-row d tiles of O^T / U^T
   constexpr int CPR = D / 8;        // 16-byte chunks per row
-  constexpr int NCH = F16_BC * CPR / NT;  // chunks per thread per tile
+  constexpr int BC = f16_bc<D>();    // keys per LDS tile
+  constexpr int NCH = BC * CPR / NT;  // chunks per thread per tile
   using SM = Fwd16Smem<D>;
   __shared__ SM sm;
 
@@ -546,7 +557,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
   const uint16_t* vp = v + ((size_t)(b * Hkv + hk) * T) * D;
 
   const int kend = min(T, q0 + BR);
-  const int ntiles = (kend + F16_BC - 1) / F16_BC;
+  const int ntiles = (kend + BC - 1) / BC;
   // 32-key sub-tiles this wave attends to: keys [0, min(kend, qw + 16))
   const int nsub = (min(kend, qw + 16) + 31) / 32;
 
@@ -555,7 +566,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
   struct Pre { u32x4 k[NCH], v[NCH]; };
   Pre preA;
   auto gload = [&](Pre& p, int key0) {
-    if (key0 + F16_BC <= T) {
+    if (key0 + BC <= T) {
       // whole tile in range: scalar tile base plus this thread's fixed offsets
       const uint16_t* kt = kp + (size_t)key0 * D;
       const uint16_t* vt = vp + (size_t)key0 * D;
@@ -742,11 +753,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd16_kernel(
   // tile j+1 and stores them into the other buffer, whose tile j-1 every wave
   // finished reading before the barrier that ended iteration j-1.
   auto iter = [&](int j, int buf) {
-    const int key0 = j * F16_BC;
-    if (j + 1 < ntiles) gload(preA, key0 + F16_BC);
+    const int key0 = j * BC;
+    if (j + 1 < ntiles) gload(preA, key0 + BC);
 #pragma unroll
-    for (int st = 0; st < F16_BC / 32; ++st)
-      if (4 * j + st < nsub) subtile(buf, buf, st, key0 + 32 * st);
+    for (int st = 0; st < BC / 32; ++st)
+      if ((BC / 32) * j + st < nsub) subtile(buf, buf, st, key0 + 32 * st);
     if (j + 1 < ntiles) lds_put(preA, buf ^ 1);
     __syncthreads();
   };
@@ -834,8 +845,10 @@ hipError_t launch_fwd(int dtype, const void* q, const void* k, const void* v, co
                       hipStream_t stream) {
   if (dtype == PLX_BF16) {
     if (d == 64)
-      return launch_fwd16<64, FWD16_WAVES>(q, k, v, rho, o, lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale, stream);
-    return launch_fwd16<128, FWD16_WAVES>(q, k, v, rho, o, lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale, stream);
+      return launch_fwd16<64, f16_waves<64>()>(q, k, v, rho, o, lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale, stream);
+    if (d == 256)
+      return launch_fwd16<256, f16_waves<256>()>(q, k, v, rho, o, lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale, stream);
+    return launch_fwd16<128, f16_waves<128>()>(q, k, v, rho, o, lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale, stream);
   }
   if (d == 64)
     return launch_fwd_t<PolF32, 64>(q, k, v, rho, o, lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale, stream);

@@ -55,7 +55,8 @@ def _fwd(**kw):
     (dict(B=0), binding.PLX_ERR_INVALID_ARG),
     (dict(Hq=3, Hkv=2), binding.PLX_ERR_INVALID_ARG),
     (dict(d=96), binding.PLX_ERR_UNSUPPORTED),
-    (dict(d=256), binding.PLX_ERR_UNSUPPORTED),
+    (dict(d=256, dtype=binding.PLX_F32), binding.PLX_ERR_UNSUPPORTED),  # d = 256: bf16 only
+    (dict(d=512), binding.PLX_ERR_UNSUPPORTED),
     (dict(scale=0.0), binding.PLX_ERR_INVALID_ARG),
     (dict(scale=float("nan")), binding.PLX_ERR_INVALID_ARG),
     (dict(dtype=7), binding.PLX_ERR_INVALID_ARG),
@@ -82,6 +83,7 @@ def _dec(**kw):
     (dict(Hq=6, Hkv=2), binding.PLX_ERR_UNSUPPORTED),  # group of 3
     (dict(Hq=5, Hkv=2), binding.PLX_ERR_INVALID_ARG),
     (dict(d=32), binding.PLX_ERR_UNSUPPORTED),
+    (dict(d=256, dtype=binding.PLX_F32), binding.PLX_ERR_UNSUPPORTED),
     (dict(ws=None), binding.PLX_ERR_WORKSPACE),
     (dict(ws_bytes=16), binding.PLX_ERR_WORKSPACE),
 ])
@@ -117,6 +119,7 @@ def _bwd(**kw):
     (dict(dr=None), binding.PLX_ERR_INVALID_ARG),
     (dict(T=-1), binding.PLX_ERR_INVALID_ARG),
     (dict(d=80), binding.PLX_ERR_UNSUPPORTED),
+    (dict(d=256), binding.PLX_ERR_UNSUPPORTED),  # the backward serves d in {64, 128}
     (dict(ws_bytes=8), binding.PLX_ERR_WORKSPACE),
     (dict(ws=None), binding.PLX_ERR_WORKSPACE),
 ])

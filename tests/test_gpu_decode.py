@@ -213,3 +213,26 @@ def test_bf16_long_decode_full_size_sampled_heads(gpu_lib):
     ref = _oracle(wl, heads)
     check_bf16(np.array([got["o"][b, h] for b, h in heads]), ref["o"], "o (sampled heads)")
     assert np.max(np.abs(np.array([got["lse"][b, h] for b, h in heads]) - ref["lse"])) <= LSE_ABS
+
+
+@pytest.mark.parametrize("G,num_splits", [(1, 0), (2, 3), (4, 0), (8, 1), (16, 0), (16, 5)])
+def test_bf16_head_dim_256(gpu_lib, G, num_splits):
+    """d = 256 on both schedules and every group size, ragged contexts
+    including a single key."""
+    say(f"case decode bf16 d256 G{G} splits={num_splits}")
+    wl = inputs.make_decode(3, 2 * G, 2, 256, 0, S_max=900, dtype="bf16", seed=90 + G,
+                            ctx_list=[900, 1, 513])
+    got = _run(wl, num_splits)
+    ref = _oracle(wl)
+    check_bf16(got["o"].reshape(-1, 256), ref["o"], "o")
+    assert np.max(np.abs(got["lse"].reshape(-1) - ref["lse"])) <= LSE_ABS
+
+
+def test_bf16_head_dim_256_key_count_probe(gpu_lib):
+    ctx = np.array([3000, 1, 257], np.int32)
+    wl = inputs.make_decode(3, 4, 2, 256, 0, S_max=3000, dtype="bf16", seed=71, ctx_list=ctx)
+    wl.tensors["q"].data[...] = 0
+    for ns in (0, 3):
+        got = _run(wl, ns)
+        n = np.rint(np.exp(got["lse"].astype(np.float64))).astype(np.int64)
+        assert np.array_equal(n, np.repeat(ctx[:, None], wl.Hq, axis=1)), ns

@@ -76,6 +76,7 @@ def _prefill(wl, flags, t=None):
     ("f32", 1, 2, 2, 67, 128),
     ("bf16", 1, 4, 2, 300, 128),
     ("bf16", 2, 2, 1, 161, 64),
+    ("bf16", 1, 2, 1, 150, 256),
 ])
 @pytest.mark.parametrize("flags", FLAGS)
 def test_prefill_family_against_oracle(gpu_lib, dtype, B, Hq, Hkv, T, d, flags):

@@ -120,3 +120,24 @@ def test_bf16_prefill_full_size_sampled_rows(gpu_lib):
     check_bf16(got_o, ref_o, "o (sampled rows)")
     assert np.max(np.abs(got_lse - ref_lse)) <= LSE_ABS
     assert T == 4096
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T", [(1, 2, 1, 200), (1, 4, 2, 129), (2, 1, 1, 64), (1, 1, 1, 1)])
+def test_bf16_head_dim_256_against_oracle(gpu_lib, B, Hq, Hkv, T):
+    """d = 256: four waves of 16 rows, 64-key tiles; several tiles and a
+    ragged tail, GQA, and the single-key row."""
+    say(f"case bf16 d256 B{B} Hq{Hq} Hkv{Hkv} T{T}")
+    wl = inputs.make_prefill(B, Hq, Hkv, T, 256, dtype="bf16", seed=61 + T, rho_std=0.1)
+    got = _run(wl, aux=True)
+    ref = _oracle(wl)
+    check_bf16(got["o"], ref["o"], "o")
+    check_bf16(got["vbar"], ref["o_sa"], "vbar")
+    assert np.max(np.abs(got["lse"] - ref["lse"])) <= LSE_ABS
+
+
+def test_key_count_probe_head_dim_256(gpu_lib):
+    wl = inputs.make_prefill(1, 2, 1, 333, 256, dtype="bf16", seed=7)
+    wl.tensors["q"].data[...] = 0
+    got = _run(wl)
+    n = np.rint(np.exp(got["lse"].astype(np.float64))).astype(np.int64)
+    assert np.array_equal(n, np.broadcast_to(np.arange(1, 334), n.shape))

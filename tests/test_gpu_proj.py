@@ -51,6 +51,7 @@ def _bounds(x, w, Hq, Hkv, d):
     (1, 300, 256, 2, 1, 64),    # N = 384: a half-filled feature tile
     (3, 100, 64, 2, 2, 128),    # one 64-deep reduction tile
     (1, 513, 1024, 4, 1, 128),  # the layer width of the projected-probe workload
+    (1, 100, 128, 2, 1, 256),   # d = 256: a head spans both feature halves of a tile
 ])
 def test_projection_against_oracle(gpu_lib, B, T, D, Hq, Hkv, d):
     say(f"case proj B{B} T{T} D{D} Hq{Hq} Hkv{Hkv} d{d}")
