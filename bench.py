@@ -279,6 +279,44 @@ def bench_proj(steps, warmup):
                          "algorithmic_flops_per_launch": flops}}
 
 
+# ------------------------------------------------------- head-dim variants
+def bench_headdim(steps, warmup):
+    """Prefill (B=4, Hq=16, Hkv=8, T=4096) and decode (B=64, Hq=16, Hkv=8,
+    ctx=8192) at d = 64 and d = 256, for comparison with the d = 128 lines."""
+    import torch
+
+    from parallax_local_linear_plx_amd import decode_workspace_size, inputs, plx_decode, plx_fwd_prefill
+
+    out = {}
+    for d in (64, 256):
+        B, Hq, Hkv, T = 4, 16, 8, 4096
+        q = inputs.device_normal((B, Hq, T, d), 1.0, 71)
+        k = inputs.device_normal((B, Hkv, T, d), 1.0, 72)
+        v = inputs.device_normal((B, Hkv, T, d), 1.0, 73)
+        rho = inputs.device_normal((B, Hq, T, d), 0.1, 74)
+        o = torch.empty((B, Hq, T, d), dtype=torch.float32, device="cuda")
+        ms = time_steps(lambda: plx_fwd_prefill(q, k, v, rho, o=o, lse=True), steps, warmup)
+        flops = 4 * 2 * d * causal_pairs(T) * B * Hq
+        del q, k, v, rho, o
+        Bd, S = 64, 8192
+        qd = inputs.device_normal((Bd, Hq, d), 1.0, 75)
+        rd = inputs.device_normal((Bd, Hq, d), 0.1, 76)
+        kc = inputs.device_normal((Bd, Hkv, S, d), 1.0, 77)
+        vc = inputs.device_normal((Bd, Hkv, S, d), 1.0, 78)
+        ctx = torch.full((Bd,), S, dtype=torch.int32, device="cuda")
+        ws = torch.empty(decode_workspace_size(Bd, Hq, Hkv, S, d, 0), dtype=torch.uint8, device="cuda")
+        od = torch.empty((Bd, Hq, d), dtype=torch.float32, device="cuda")
+        msd = time_steps(lambda: plx_decode(qd, rd, kc, vc, ctx, num_splits=0, workspace=ws, o=od), steps, warmup)
+        nbytes = Bd * Hkv * S * d * 4 + Bd * Hq * d * 8
+        del qd, rd, kc, vc, ws, od
+        torch.cuda.empty_cache()
+        out[f"d{d}"] = {"prefill_us": ms * 1e3, "prefill_tflops": flops / (ms * 1e-3) / 1e12,
+                        "prefill_mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                        "decode_us": msd * 1e3, "decode_GB/s": nbytes / (msd * 1e-3) / 1e9,
+                        "decode_hbm_frac": nbytes / (msd * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    return out
+
+
 # -------------------------------------------------------- copy calibration
 def bench_copy(steps, nbytes=1 << 30):
     """A plain device-to-device copy of a known size.  Run under rocprofv3
@@ -376,7 +414,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--only", default="all",
                     choices=["all", "prefill", "decode", "decode_long", "train", "proj", "copy",
-                             "decode_sweep"])
+                             "decode_sweep", "headdim"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay decode timing")
     args = ap.parse_args()
@@ -402,6 +440,13 @@ def main():
         log(f"  {res['prefill']['ms'] * 1e3:.1f} us  {res['prefill']['tflops']:.1f} TFLOP/s")
     if args.only == "copy":
         print(json.dumps(bench_copy(args.steps)), flush=True)
+        return
+    if args.only == "headdim":
+        log("head-dim variants ...")
+        print(json.dumps({"metric": "prefill TFLOP/s and decode GB/s at d = 64 and 256", "n_gpus": 1,
+                          "dtype": "bf16", "data": "synthetic",
+                          "headdim": bench_headdim(max(10, args.steps // 2), max(10, args.warmup // 2))}),
+              flush=True)
         return
     if args.only == "decode_sweep":
         log("decode sweep (batch x context) ...")
