@@ -18,7 +18,8 @@
 // exactly (kbar = sum_j w_j k_j), so the scalar C carries everything of the
 // mean key the output needs, and it merges across ranges like l.
 // Kernel 2 (merge): per (b, h) rescales the records to a common max and
-// finishes  o = (O/l)(1 + C/l) - U/l,  LSE = M + ln l.
+// finishes  o = (O/l)(1 + C/l) - U/l,  LSE = M + ln e  (and, on request, the
+// no-intercept output -U/l and the correction-to-output ratio).
 #include "plx_common.hpp"
 #include "plx_kernels.hpp"
 
