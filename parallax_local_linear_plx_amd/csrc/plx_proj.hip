@@ -12,12 +12,14 @@
 // Kernel: 256 x 256 output tiles (tokens x features), eight waves, two per
 // SIMD, each owning 128 features x 64 tokens of the tile as 4 x 2 accumulators
 // of the 32x32x16 bf16 MFMA (fp32).  64-deep W and X tiles are
-// double-buffered in LDS; the global loads of tile t+1 are issued at the start
-// of tile t and stored at its end.  The operands of each 16-deep step are read
-// from LDS while the previous step's MFMAs run; at a tile boundary the barrier
-// and the first reads of the next tile sit before the last step's MFMAs.  The
-// epilogue rounds to bf16 (round to nearest even), transposes each wave's tile
-// through LDS and stores whole rows of d, one head per 16-lane group.
+// double-buffered in LDS and loaded straight into it (global_load_lds, no
+// register staging) in an XOR-swizzled layout that keeps the operand reads
+// free of bank conflicts; tile t+1 is requested at the start of tile t.  The
+// operands of each 16-deep step are read from LDS while the previous step's
+// MFMAs run; at a tile boundary the barrier and the first reads of the next
+// tile sit before the last step's MFMAs.  The epilogue rounds to bf16 (round
+// to nearest even), transposes each wave's tile through LDS and stores whole
+// rows of d, one head per 16-lane group.
 #include "plx_common.hpp"
 #include "plx_kernels.hpp"
 
@@ -29,9 +31,10 @@ constexpr int PJ_BM = 256;      // tokens per workgroup
 constexpr int PJ_BN = 256;      // output features per workgroup
 constexpr int PJ_BK = 64;       // reduction depth of one LDS tile
 constexpr int PJ_THREADS = 512;
-constexpr int PJ_LD = PJ_BK + 8;  // LDS row stride (elements): 144 B, conflict-free b128 reads
+constexpr int PJ_LD = PJ_BK;  // LDS row stride (elements): 128 B, chunks XOR-swizzled
 constexpr int PJ_OLD = 128 + 8;   // epilogue row stride (elements)
-constexpr int PJ_CH = PJ_BM * PJ_BK / 8 / PJ_THREADS;  // 16-byte chunks per thread per operand tile
+// the loads cover a tile as 8 waves x 4 instructions x 8 rows
+static_assert(PJ_THREADS / 64 * 4 * 8 == PJ_BM && PJ_BM == PJ_BN, "tile load coverage");
 
 struct ProjSmem {
   union {
@@ -66,33 +69,33 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_kernel(
   const int wn = wave & 1, wm = wave >> 1;  // wave tile: features wn*128.., tokens wm*64..
   const int l32 = lane & 31, h = lane >> 5;
 
-  // global -> register staging of one 64-deep tile of W and X (rows past the
-  // end read the last row: finite, and their results are never stored)
-  u32x4 sw[PJ_CH], sx[PJ_CH];
-  auto gload = [&](int k0) {
+  // Global -> LDS without registers: each wave's load instruction fills 8
+  // rows (1 KB) of a tile; lane l writes 16-byte chunk l % 8 of row l / 8.
+  // Physical chunk p of row r holds logical chunk p ^ ((r >> 1) & 7), which
+  // spreads the 16 rows one operand read touches over all 64 banks.
+  auto gload = [&](int buf, int k0) {
 #pragma unroll
-    for (int i = 0; i < PJ_CH; ++i) {
-      const int it = threadIdx.x + PJ_THREADS * i;
-      const int row = it >> 3, c = (it & 7) * 8;
-      sw[i] = *reinterpret_cast<const u32x4*>(w + (size_t)min(n0 + row, N - 1) * K + k0 + c);
-      sx[i] = *reinterpret_cast<const u32x4*>(x + (size_t)min(m0 + row, M - 1) * K + k0 + c);
-    }
-  };
-  auto lds_put = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < PJ_CH; ++i) {
-      const int it = threadIdx.x + PJ_THREADS * i;
-      const int row = it >> 3, c = (it & 7) * 8;
-      *reinterpret_cast<u32x4*>(&sm.in.w[buf][row * PJ_LD + c]) = sw[i];
-      *reinterpret_cast<u32x4*>(&sm.in.x[buf][row * PJ_LD + c]) = sx[i];
+    for (int j = 0; j < 4; ++j) {
+      const int blk = wave * 4 + j;           // 8-row block of the 256-row tile
+      const int row = blk * 8 + (lane >> 3);
+      const int lc = (lane & 7) ^ ((row >> 1) & 7);
+      const uint16_t* gw = w + (size_t)min(n0 + row, N - 1) * K + k0 + 8 * lc;
+      const uint16_t* gx = x + (size_t)min(m0 + row, M - 1) * K + k0 + 8 * lc;
+      __builtin_amdgcn_global_load_lds((const void*)gw,
+          (__attribute__((address_space(3))) void*)&sm.in.w[buf][blk * 8 * PJ_LD], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)gx,
+          (__attribute__((address_space(3))) void*)&sm.in.x[buf][blk * 8 * PJ_LD], 16, 0, 0);
     }
   };
   // operands of one 16-deep step: A = W rows (features), B = X rows (tokens);
   // lane (l32, h) supplies row l32 of each 32-row block and depth 8h .. 8h+7
+  // (logical chunk 2 ks + h; the swizzle depends only on l32)
   struct Ops { bf16x8 a[4], b[2]; };
+  const int swz = (l32 >> 1) & 7;
   auto read_ops = [&](Ops& o, int buf, int ks) {
-    const uint16_t* wr = &sm.in.w[buf][(wn * 128 + l32) * PJ_LD + 16 * ks + 8 * h];
-    const uint16_t* xr = &sm.in.x[buf][(wm * 64 + l32) * PJ_LD + 16 * ks + 8 * h];
+    const int pc = (2 * ks + h) ^ swz;
+    const uint16_t* wr = &sm.in.w[buf][(wn * 128 + l32) * PJ_LD + 8 * pc];
+    const uint16_t* xr = &sm.in.x[buf][(wm * 64 + l32) * PJ_LD + 8 * pc];
 #pragma unroll
     for (int i = 0; i < 4; ++i) o.a[i] = *reinterpret_cast<const bf16x8*>(wr + 32 * i * PJ_LD);
 #pragma unroll
@@ -113,15 +116,17 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_kernel(
   };
 
   const int ntiles = K / PJ_BK;
-  gload(0);
-  lds_put(0);
+  gload(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   Ops cur, nxt;
   read_ops(cur, 0, 0);
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     const bool more = t + 1 < ntiles;
-    if (more) gload((t + 1) * PJ_BK);
+    // tile t+1 into the other buffer, whose tile t-1 every wave finished
+    // reading before the barrier that ended tile t-1
+    if (more) gload(buf ^ 1, (t + 1) * PJ_BK);
 #pragma unroll
     for (int ks = 0; ks < PJ_BK / 16 - 1; ++ks) {
       read_ops(nxt, buf, ks + 1);
@@ -130,10 +135,9 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_kernel(
       __builtin_amdgcn_sched_barrier(0);
       cur = nxt;
     }
-    // last step of the tile: stage tile t+1 into the other buffer (its tile
-    // t-1 was read before the previous barrier), make it visible, start
-    // reading its first step, then issue this step's MFMAs
-    if (more) lds_put(buf ^ 1);
+    // last step: wait for tile t+1, make it visible, start reading it, then
+    // issue this step's MFMAs
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (more) read_ops(nxt, buf ^ 1, 0);
     __builtin_amdgcn_sched_barrier(0);
