@@ -578,18 +578,67 @@ __device__ __forceinline__ void wave_merge(const float* __restrict__ rec0, size_
                                            float* __restrict__ lse_out, float* __restrict__ cor_out) {
   constexpr int EPL = D / 64;
   const int lane = threadIdx.x & 63;
-  float M = -INFINITY;
-  for (int i = lane; i < n; i += 64)
-    if (valid(i)) M = fmaxf(M, rec0[(size_t)i * stride]);
+  // O and U rows of eight records, loaded together; past the end the last
+  // record is read again (it gets weight zero)
+  auto load8 = [&](int first, float (&ov)[8][EPL], float (&uv)[8][EPL]) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    for (int j = 0; j < 8; ++j) {
+      const float* r = rec0 + (size_t)min(first + j, n - 1) * stride + 4 + lane * EPL;
+      if constexpr (EPL == 4) {
+        const float4 o4 = *reinterpret_cast<const float4*>(r);
+        const float4 u4 = *reinterpret_cast<const float4*>(r + D);
+        ov[j][0] = o4.x, ov[j][1] = o4.y, ov[j][2] = o4.z, ov[j][3] = o4.w;
+        uv[j][0] = u4.x, uv[j][1] = u4.y, uv[j][2] = u4.z, uv[j][3] = u4.w;
+      } else if constexpr (EPL == 2) {
+        const float2 o2 = *reinterpret_cast<const float2*>(r);
+        const float2 u2 = *reinterpret_cast<const float2*>(r + D);
+        ov[j][0] = o2.x, ov[j][1] = o2.y, uv[j][0] = u2.x, uv[j][1] = u2.y;
+      } else {
+        ov[j][0] = r[0], uv[j][0] = r[D];
+      }
+    }
+  };
   float l = 0.f, e = 0.f, C = 0.f, O[EPL], U[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) O[j] = U[j] = 0.f;
+  // a record that was never written (weight 0) may hold anything: selects,
+  // not products, keep it out
+  auto accum8 = [&](float a, int k0, int cnt, const float (&ov)[8][EPL], const float (&uv)[8][EPL]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + j;
+      const float ak = k < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), k & 63)) : 0.f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        O[i] = ak != 0.f ? __builtin_fmaf(ak, ov[j][i], O[i]) : O[i];
+        U[i] = ak != 0.f ? __builtin_fmaf(ak, uv[j][i], U[i]) : U[i];
+      }
+    }
+  };
+
+  // Records 0..63: one header per lane, and the rows of records 0..7, all
+  // requested before the max is known (one round trip for most heads).
+  float4 hdr = {-INFINITY, 0.f, 0.f, 0.f};
+  const bool mine = lane < n && valid(lane);
+  if (lane < n) hdr = *reinterpret_cast<const float4*>(rec0 + (size_t)lane * stride);
+  float ov[8][EPL], uv[8][EPL];
+  load8(0, ov, uv);
+  float M = mine ? hdr.x : -INFINITY;
+  for (int i = lane + 64; i < n; i += 64)
+    if (valid(i)) M = fmaxf(M, rec0[(size_t)i * stride]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
   for (int base = 0; base < n; base += 64) {
     const int i = base + lane;
     float a = 0.f;
-    if (i < n && valid(i)) {
+    if (base == 0) {
+      if (mine) {
+        a = fast_exp2(hdr.x - M);
+        l += a * hdr.y;
+        e += a * hdr.z;
+        C += a * hdr.w;
+      }
+    } else if (i < n && valid(i)) {
       const float* r = rec0 + (size_t)i * stride;
       a = fast_exp2(r[0] - M);
       l += a * r[1];
@@ -598,35 +647,8 @@ __device__ __forceinline__ void wave_merge(const float* __restrict__ rec0, size_
     }
     const int cnt = min(64, n - base);
     for (int k0 = 0; k0 < cnt; k0 += 8) {
-      // eight records per step, loads first; past the end the last record is
-      // read again with weight zero
-      float ak[8], ov[8][EPL], uv[8][EPL];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int k = k0 + j;
-        ak[j] = k < cnt ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), k & 63)) : 0.f;
-        const float* r = rec0 + (size_t)min(base + k, n - 1) * stride + 4 + lane * EPL;
-        if constexpr (EPL == 4) {
-          const float4 o4 = *reinterpret_cast<const float4*>(r);
-          const float4 u4 = *reinterpret_cast<const float4*>(r + D);
-          ov[j][0] = o4.x, ov[j][1] = o4.y, ov[j][2] = o4.z, ov[j][3] = o4.w;
-          uv[j][0] = u4.x, uv[j][1] = u4.y, uv[j][2] = u4.z, uv[j][3] = u4.w;
-        } else if constexpr (EPL == 2) {
-          const float2 o2 = *reinterpret_cast<const float2*>(r);
-          const float2 u2 = *reinterpret_cast<const float2*>(r + D);
-          ov[j][0] = o2.x, ov[j][1] = o2.y, uv[j][0] = u2.x, uv[j][1] = u2.y;
-        } else {
-          ov[j][0] = r[0], uv[j][0] = r[D];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-          // a record that was never written (weight 0) may hold anything
-          O[i] = ak[j] != 0.f ? __builtin_fmaf(ak[j], ov[j][i], O[i]) : O[i];
-          U[i] = ak[j] != 0.f ? __builtin_fmaf(ak[j], uv[j][i], U[i]) : U[i];
-        }
+      if (base != 0 || k0 != 0) load8(base + k0, ov, uv);
+      accum8(a, k0, cnt, ov, uv);
     }
   }
 #pragma unroll
