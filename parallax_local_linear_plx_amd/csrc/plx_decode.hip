@@ -40,11 +40,11 @@ struct DecSmem {
   static constexpr size_t TILE_BYTES = (size_t)DEC_WAVES * 2 * D * DEC_TLD * sizeof(vel_t);
   union {
     vel_t tiles[DEC_WAVES][D * DEC_TLD];  // per wave: V^T
-    float merge[32 * MLD];                // [O | U] x column x d
+    float merge[DEC_WAVES][32 * MLD];     // per wave: [O | U] x column x d
   };
   float mw[DEC_WAVES][32];
-  float lsum[32];
-  float esum[32];
+  float wl[DEC_WAVES][32];  // per wave: l (even columns) / C (odd columns)
+  float we[DEC_WAVES][32];  // per wave: e
 };
 
 __device__ __forceinline__ float dpp_even_partner(float x) {
@@ -199,14 +199,12 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
     wave_lds_sync();
   }
 
-  // ---- merge the four waves' states through LDS ----
+  // ---- merge the four waves' states through LDS: each wave stores its
+  // rescaled state in its own slot and the record sums the slots in wave
+  // order, so the result does not depend on timing ----
+  constexpr int MLD = DecSmem<Pol, D>::MLD;
   __syncthreads();
   if (half == 0) sm.mw[wave][col] = m_run;
-  for (int i = threadIdx.x; i < 32 * DecSmem<Pol, D>::MLD; i += DEC_THREADS) sm.merge[i] = 0.f;
-  if (threadIdx.x < 32) {
-    sm.lsum[threadIdx.x] = 0.f;
-    sm.esum[threadIdx.x] = 0.f;
-  }
   __syncthreads();
   float M = -INFINITY;
 #pragma unroll
@@ -215,15 +213,15 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
   const float l_tot = (l_part + xor32(l_part)) * sc;
   const float e_tot = (e_part + xor32(e_part)) * sc;
   if (half == 0) {
-    atomicAdd(&sm.lsum[col], l_tot);
-    atomicAdd(&sm.esum[col], e_tot);
+    sm.wl[wave][col] = l_tot;
+    sm.we[wave][col] = e_tot;
   }
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
     for (int a = 0; a < 16; ++a) {
       const int d = 32 * dt + acc_row(a, half);
-      atomicAdd(&sm.merge[col * DecSmem<Pol, D>::MLD + d], ou[dt][a] * sc);
+      sm.merge[wave][col * MLD + d] = ou[dt][a] * sc;
     }
   __syncthreads();
 
@@ -233,16 +231,27 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
     float* rec = part + (((size_t)b * Hq + hk * G + g) * nsplit + split) * REC;
     const int c0 = 2 * g;
     if (threadIdx.x == 0) {
-      float M0 = -INFINITY;
-      for (int w = 0; w < DEC_WAVES; ++w) M0 = fmaxf(M0, sm.mw[w][c0]);
+      float M0 = -INFINITY, l0 = 0.f, e0 = 0.f, C0 = 0.f;
+      for (int w = 0; w < DEC_WAVES; ++w) {
+        M0 = fmaxf(M0, sm.mw[w][c0]);
+        l0 += sm.wl[w][c0];
+        e0 += sm.we[w][c0];
+        C0 += sm.wl[w][c0 + 1];
+      }
       rec[0] = M0;
-      rec[1] = sm.lsum[c0];
-      rec[2] = sm.esum[c0];
-      rec[3] = sm.lsum[c0 + 1];
+      rec[1] = l0;
+      rec[2] = e0;
+      rec[3] = C0;
     }
     for (int d = threadIdx.x; d < D; d += DEC_THREADS) {
-      rec[4 + d] = sm.merge[c0 * DecSmem<Pol, D>::MLD + d];
-      rec[4 + D + d] = sm.merge[(c0 + 1) * DecSmem<Pol, D>::MLD + d];
+      float od = 0.f, ud = 0.f;
+#pragma unroll
+      for (int w = 0; w < DEC_WAVES; ++w) {
+        od += sm.merge[w][c0 * MLD + d];
+        ud += sm.merge[w][(c0 + 1) * MLD + d];
+      }
+      rec[4 + d] = od;
+      rec[4 + D + d] = ud;
     }
   }
 }
@@ -288,12 +297,12 @@ struct Dec16Smem {
   static constexpr int MLD = D + 1;
   union {
     uint16_t tiles[DEC_WAVES][TILE];  // per wave: raw bf16 V rows
-    float merge[16 * MLD];            // [O | U] x column x d
+    float merge[DEC_WAVES][16 * MLD]; // per wave: [O | U] x column x d
   };
   uint16_t bq[16 * D];  // score B operand: [column][d]
   float mw[DEC_WAVES][16];
-  float lsum[16];
-  float esum[16];
+  float wl[DEC_WAVES][16];  // per wave: l (even columns) / C (odd columns)
+  float we[DEC_WAVES][16];  // per wave: e
 };
 
 __device__ __forceinline__ s16x4_t tr16raw(const uint16_t* p) {
@@ -497,14 +506,10 @@ __device__ __forceinline__ void dec16_range(Dec16Smem<D>& sm, const uint16_t* __
     for (int i = 0; i < DEC_NSET; ++i) process(kr[i], vr[i], key0 + i * DEC_GROUP_KEYS);
   }
 
-  // ---- merge the four waves' states through LDS ----
+  // ---- merge the four waves' states through LDS (each wave its own slot,
+  // summed in wave order: the record does not depend on timing) ----
   __syncthreads();
   if (g == 0) sm.mw[wave][c] = m_run;
-  for (int i = threadIdx.x; i < 16 * SM::MLD; i += DEC_THREADS) sm.merge[i] = 0.f;
-  if (threadIdx.x < 16) {
-    sm.lsum[threadIdx.x] = 0.f;
-    sm.esum[threadIdx.x] = 0.f;
-  }
   __syncthreads();
   float M = -INFINITY;
 #pragma unroll
@@ -516,15 +521,15 @@ __device__ __forceinline__ void dec16_range(Dec16Smem<D>& sm, const uint16_t* __
   et += __shfl_xor(et, 16, 64);
   et += __shfl_xor(et, 32, 64);
   if (g == 0) {
-    atomicAdd(&sm.lsum[c], lt * sc);
-    atomicAdd(&sm.esum[c], et * sc);
+    sm.wl[wave][c] = lt * sc;
+    sm.we[wave][c] = et * sc;
   }
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d = 16 * dt + 4 * g + j;
-      atomicAdd(&sm.merge[c * SM::MLD + d], ou[dt][j] * sc);
+      sm.merge[wave][c * SM::MLD + d] = ou[dt][j] * sc;
     }
   __syncthreads();
 
@@ -532,16 +537,27 @@ __device__ __forceinline__ void dec16_range(Dec16Smem<D>& sm, const uint16_t* __
     float* r = rec + hh * rec_stride;
     const int c0 = 2 * hh;
     if (threadIdx.x == 0) {
-      float M0 = -INFINITY;
-      for (int w = 0; w < DEC_WAVES; ++w) M0 = fmaxf(M0, sm.mw[w][c0]);
+      float M0 = -INFINITY, l0 = 0.f, e0 = 0.f, C0 = 0.f;
+      for (int w = 0; w < DEC_WAVES; ++w) {
+        M0 = fmaxf(M0, sm.mw[w][c0]);
+        l0 += sm.wl[w][c0];
+        e0 += sm.we[w][c0];
+        C0 += sm.wl[w][c0 + 1];
+      }
       r[0] = M0;
-      r[1] = sm.lsum[c0];
-      r[2] = sm.esum[c0];
-      r[3] = sm.lsum[c0 + 1];
+      r[1] = l0;
+      r[2] = e0;
+      r[3] = C0;
     }
     for (int d = threadIdx.x; d < D; d += DEC_THREADS) {
-      r[4 + d] = sm.merge[c0 * SM::MLD + d];
-      r[4 + D + d] = sm.merge[(c0 + 1) * SM::MLD + d];
+      float od = 0.f, ud = 0.f;
+#pragma unroll
+      for (int w = 0; w < DEC_WAVES; ++w) {
+        od += sm.merge[w][c0 * SM::MLD + d];
+        ud += sm.merge[w][(c0 + 1) * SM::MLD + d];
+      }
+      r[4 + d] = od;
+      r[4 + D + d] = ud;
     }
   }
   __syncthreads();  // the next range reuses the LDS tiles that alias the merge buffer

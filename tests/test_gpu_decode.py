@@ -236,3 +236,16 @@ def test_bf16_head_dim_256_key_count_probe(gpu_lib):
         got = _run(wl, ns)
         n = np.rint(np.exp(got["lse"].astype(np.float64))).astype(np.int64)
         assert np.array_equal(n, np.repeat(ctx[:, None], wl.Hq, axis=1)), ns
+
+
+@pytest.mark.parametrize("num_splits,dtype", [(0, "bf16"), (3, "bf16"), (2, "f32")])
+def test_repeat_runs_are_bitwise_identical(gpu_lib, num_splits, dtype):
+    """The four waves of a workgroup combine their states in a fixed order and
+    the merge sums records in slot order: repeated calls agree bit for bit."""
+    wl = inputs.make_decode(5, 8, 2, 128, 0, S_max=3000, dtype=dtype, seed=130,
+                            ctx_list=[3000, 1, 777, 2048, 129])
+    t = _dev(wl)
+    a = _run(wl, num_splits, t)
+    for _ in range(3):
+        b = _run(wl, num_splits, t)
+        assert np.array_equal(a["o"], b["o"]) and np.array_equal(a["lse"], b["lse"])

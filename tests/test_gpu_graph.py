@@ -1,0 +1,95 @@
+"""The entry points captured in a HIP graph (through torch.cuda.CUDAGraph) and
+replayed: every replay, with new inputs copied in between and eager work and
+synchronisations around it, must reproduce the eager call bit for bit.  The
+library launches kernels only (no memset or copy nodes), so a captured call
+is the same kernel sequence as an eager one."""
+
+import numpy as np
+import pytest
+
+from parallax_local_linear_plx_amd import inputs
+from tests._util import say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _capture(fn):
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # warm-up outside the graph (loads the library, allocates nothing new)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_decode_graph_replays_match_eager(gpu_lib, num_splits):
+    import torch
+
+    from parallax_local_linear_plx_amd import decode_workspace_size, plx_decode
+
+    B, Hq, Hkv, d, S = 3, 8, 2, 128, 700
+    say(f"case decode graph replay splits={num_splits}")
+    wl = inputs.make_decode(B, Hq, Hkv, d, 0, S_max=S, dtype="bf16", seed=120, ctx_list=[700, 1, 333])
+    t = {n: to_device(x) for n, x in wl.tensors.items()}
+    q = t["q"].reshape(B, Hq, d).clone()
+    rho = t["rho"].reshape(B, Hq, d).clone()
+    ctx = torch.from_numpy(wl.ctx_len).cuda()
+    ws = torch.empty(decode_workspace_size(B, Hq, Hkv, S, d, num_splits), dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+
+    def call():
+        out = plx_decode(q, rho, t["k"], t["v"], ctx, wl.scale, num_splits=num_splits, workspace=ws, o=o,
+                         lse=True)
+        lse.copy_(out["lse"])
+
+    g = _capture(call)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    for rep in range(4):
+        q.copy_(torch.randn(q.shape, generator=gen, device="cuda").bfloat16())
+        rho.copy_((0.1 * torch.randn(rho.shape, generator=gen, device="cuda")).bfloat16())
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = o.clone(), lse.clone()
+        ws.fill_(0xFF)  # eager work between replays, and a dirty workspace
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(got_o, o) and torch.equal(got_l, lse), f"replay {rep} differs from eager"
+    del g
+
+
+def test_prefill_graph_replays_match_eager(gpu_lib):
+    import torch
+
+    from parallax_local_linear_plx_amd import plx_fwd_prefill
+
+    wl = inputs.make_prefill(1, 4, 2, 300, 128, dtype="bf16", seed=121)
+    t = {n: to_device(x).clone() for n, x in wl.tensors.items()}
+    o = torch.empty((1, 4, 300, 128), dtype=torch.float32, device="cuda")
+
+    def call():
+        plx_fwd_prefill(t["q"], t["k"], t["v"], t["rho"], wl.scale, o=o, lse=False)
+
+    g = _capture(call)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(6)
+    for rep in range(3):
+        t["q"].copy_(torch.randn(t["q"].shape, generator=gen, device="cuda").bfloat16())
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = o.clone()
+        o.zero_()
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(got, o), f"replay {rep} differs from eager"
+    del g
