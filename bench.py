@@ -341,12 +341,18 @@ KERNEL_SOURCES = {
 
 
 def source_digest(key):
+    """Digest of the kernel sources with comments and whitespace removed, so
+    that only a change to the code itself invalidates a counter summary."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[key]:
-        with open(os.path.join(ROOT, "parallax_local_linear_plx_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "parallax_local_linear_plx_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

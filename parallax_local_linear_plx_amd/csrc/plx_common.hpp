@@ -8,6 +8,9 @@
 //     (half, element); the kernels choose that assignment themselves.
 //   * C/D (32 x 32, 16 fp32 per lane): acc[4*i + j] is row 8*i + 4*h + j,
 //     column l % 32.
+//   * 16x16 tiles (the bf16 prefill, decode and backward kernels): operands
+//     give lane l row / column l % 16 and K-chunk l / 16; acc[j] is row
+//     4 * (l / 16) + j, column l % 16.
 // "Transposed" scoring (S^T = K Q^T) therefore puts one query per lane column
 // and that query's keys along the accumulator, so row statistics (max, sums,
 // rescale factors) stay inside a lane plus one exchange between lane halves,
