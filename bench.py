@@ -317,6 +317,66 @@ def bench_headdim(steps, warmup):
     return out
 
 
+# ------------------------------------------------------- measured ceilings
+def measured_peaks(reps=10):
+    """Ceilings measured on this GPU, reported beside the published peaks:
+    the bf16 rate of independent 16x16x32 MFMA chains with nothing else in the
+    loop (1024 workgroups of four waves), and the best HBM read rate of a
+    streaming kernel (32 KB tiles, eight 16-byte loads in flight per thread,
+    1024 to 8192 workgroups) over a 2 GiB buffer, above the 256 MB last-level
+    cache.  Both kernels live in libplx_peak.so."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "parallax_local_linear_plx_amd", "libplx_peak.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with python -m parallax_local_linear_plx_amd.build")
+    L = ctypes.CDLL(path)
+    L.plx_peak_mfma_flops.restype = ctypes.c_double
+    L.plx_peak_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.plx_peak_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.plx_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = torch.empty(4096, dtype=torch.float32, device="cuda")
+
+    def best_ms(fn):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            fn()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e))
+        return min(ts)
+
+    blocks, iters = 1024, 500
+
+    def mfma():
+        if L.plx_peak_mfma_bf16(ctypes.c_void_p(out.data_ptr()), blocks, iters, stream) != 0:
+            raise RuntimeError("plx_peak_mfma_bf16 failed")
+    tflops = L.plx_peak_mfma_flops(blocks, iters) / (best_ms(mfma) * 1e-3) / 1e12
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    gbs = 0.0
+    for nb in (1024, 2048, 4096, 8192):
+        def read(nb=nb):
+            if L.plx_peak_hbm_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
+                                   nb, stream) != 0:
+                raise RuntimeError("plx_peak_hbm_read failed")
+        gbs = max(gbs, nbytes / (best_ms(read) * 1e-3) / 1e9)
+    del buf
+    return {"mfma_bf16_tflops": round(tflops, 1), "hbm_read_gbs": round(gbs, 1),
+            "mfma_kernel": "mfma_peak_kernel: 8 independent v_mfma_f32_16x16x32_bf16 chains per wave",
+            "hbm_kernel": "hbm_read_kernel: 32 KB tiles of 16-byte loads over 2 GiB"}
+
+
 # -------------------------------------------------------- copy calibration
 def bench_copy(steps, nbytes=1 << 30):
     """A plain device-to-device copy of a known size.  Run under rocprofv3
@@ -420,7 +480,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--only", default="all",
                     choices=["all", "prefill", "decode", "decode_long", "train", "proj", "copy",
-                             "decode_sweep", "headdim"])
+                             "decode_sweep", "headdim", "peaks"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay decode timing")
     args = ap.parse_args()
@@ -446,6 +506,9 @@ def main():
         log(f"  {res['prefill']['ms'] * 1e3:.1f} us  {res['prefill']['tflops']:.1f} TFLOP/s")
     if args.only == "copy":
         print(json.dumps(bench_copy(args.steps)), flush=True)
+        return
+    if args.only == "peaks":
+        print(json.dumps(measured_peaks()), flush=True)
         return
     if args.only == "headdim":
         log("head-dim variants ...")
@@ -485,6 +548,12 @@ def main():
         res["train"] = bench_train(max(3, args.steps // 4), max(1, args.warmup // 2))
         log(f"  fwd {res['train']['fwd_ms']:.2f} ms  bwd {res['train']['bwd_ms']:.2f} ms")
 
+    peaks = None
+    if args.only == "all":
+        log("measured ceilings ...")
+        peaks = measured_peaks()
+        log(f"  MFMA bf16 {peaks['mfma_bf16_tflops']:.0f} TFLOP/s, HBM read {peaks['hbm_read_gbs']:.0f} GB/s")
+
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded device draws, q,k,v~N(0,1), rho=W_R x / N(0,0.1^2))"}
@@ -497,6 +566,9 @@ def main():
                                   "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4),
                                   "traffic": measured_traffic("prefill"),
                                   "kernel": "fwd16_kernel<128,8>",
+                                  **({"measured_peak": peaks["mfma_bf16_tflops"],
+                                      "frac_of_measured": round(p["tflops"] / peaks["mfma_bf16_tflops"], 4)}
+                                     if peaks else {}),
                                   "algorithmic_flops_per_launch": p["flops"]}})
     else:
         line.update({"value": None, "unit": "TFLOP/s", "ms_per_step": None, "config": {"workload": args.only}})
@@ -510,7 +582,11 @@ def main():
                     "unit": "GB/s", "frac": round(r["GB/s"] / PEAK_HBM_GBS, 4),
                     "traffic": measured_traffic("decode") if key == "decode" else None,
                     "kernel": "decode16_balanced_kernel<128,2> + decode_merge_balanced_kernel<128>",
+                    **({"measured_peak": peaks["hbm_read_gbs"],
+                        "frac_of_measured": round(r["GB/s"] / peaks["hbm_read_gbs"], 4)} if peaks else {}),
                     "algorithmic_bytes_per_launch": r["bytes"]}
+    if peaks:
+        line["measured_peaks"] = peaks
     if not args.no_cpu and args.only in ("all", "prefill"):
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline()

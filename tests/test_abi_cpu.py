@@ -30,6 +30,24 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert hasattr(L, n), f"symbol {n} declared in plx.h but not exported"
 
 
+def test_ceiling_library_loads_and_validates_arguments():
+    """libplx_peak.so (the benchmark's measured ceilings) is built beside
+    libplx.so; its entry points reject bad arguments before any launch."""
+    path = os.path.join(ROOT, "parallax_local_linear_plx_amd", "libplx_peak.so")
+    L = ctypes.CDLL(path)
+    L.plx_peak_mfma_flops.restype = ctypes.c_double
+    L.plx_peak_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    assert L.plx_peak_mfma_flops(1024, 500) == 1024 * 4 * 500 * 8 * 2 * 16 * 16 * 32
+    L.plx_peak_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert L.plx_peak_mfma_bf16(None, 1, 1, None) == 1
+    assert L.plx_peak_mfma_bf16(FAKE, 0, 1, None) == 1
+    L.plx_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_void_p]
+    assert L.plx_peak_hbm_read(FAKE, 24, FAKE, 1, None) == 1  # not a multiple of 16
+    assert L.plx_peak_hbm_read(ctypes.c_void_p(0x10008), 32, FAKE, 1, None) == 1  # misaligned
+    assert L.plx_peak_hbm_read(None, 32, FAKE, 1, None) == 1
+
+
 def test_abi_version_and_status_strings():
     L = binding.lib()
     assert L.plx_abi_version() == 1
