@@ -948,10 +948,13 @@ int decode_chunk_keys(int S_max, int num_splits) {
 size_t decode_record_floats(int d) { return 2 * (size_t)d + 4; }
 
 // Workgroups of the balanced schedule: two per compute unit, fewer when the
-// cache holds under ~1024 keys per workgroup.
+// cache holds under ~512 keys per workgroup.  Small caches are latency-bound
+// (each 128-key step of a workgroup waits for its loads), so they take short
+// ranges: 512 keys per workgroup measured 16-20 us per call where 1024 took
+// 22-24 us (B = 1..16, 1K-4K keys); 256 was no better overall.
 int decode_balanced_ctas(int B, int Hkv, int S_max) {
   const long long keys = (long long)B * Hkv * S_max;
-  long long p = (keys + 1023) / 1024;
+  long long p = (keys + 511) / 512;
   if (p > DEC_BAL_CTAS) p = DEC_BAL_CTAS;
   return p < 1 ? 1 : (int)p;
 }
