@@ -145,6 +145,28 @@ def test_bwd_validation(kw, status):
     assert _bwd(**kw) == status
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,S_max,d", [
+    (64, 16, 8, 8192, 128),   # 512 workgroups
+    (1, 16, 8, 1024, 128),    # 16 workgroups of 512 keys
+    (3, 4, 2, 700, 64),       # ceil(4200 / 512) = 9
+    (1, 1, 1, 1, 256),        # a single workgroup
+])
+def test_balanced_decode_workspace_follows_the_schedule(B, Hq, Hkv, S_max, d):
+    """The automatic schedule's workspace covers both automatic schedules:
+    the balanced one (bf16) keeps one record of 2d + 4 floats per query head
+    for each of the P + B Hkv (workgroup, segment) pieces, with
+    P = min(512, ceil(B Hkv S_max / 512)) workgroups; the automatic split
+    count (fp32) takes min(ceil(512 / (B Hkv)), ceil(S_max / 256)) splits of
+    whole 128-key steps, one record per (b, query head, split)."""
+    rec = (2 * d + 4) * 4
+    P = min(512, -(-B * Hkv * S_max // 512))
+    balanced = (P + B * Hkv) * (Hq // Hkv) * rec
+    ns = max(1, min(-(-512 // (B * Hkv)), -(-S_max // 256)))
+    chunk = -(-(-(-S_max // ns)) // 128) * 128
+    split = B * Hq * -(-S_max // chunk) * rec
+    assert binding.decode_workspace_size(B, Hq, Hkv, S_max, d, 0) == max(balanced, split)
+
+
 def test_bwd_workspace_size():
     # G and delta (fp32 per query row, padded to 256 bytes), then fp16 copies of
     # q, rho, dO ([B, Hq, T, d]) and k, v ([B, Hkv, T, d])
