@@ -41,10 +41,37 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def time_steps(fn, steps, warmup):
-    """Average ms per call of fn over `steps` timed calls (after `warmup`)."""
+# The GPU raises its clocks only under sustained work (about 40 ms on the
+# MI355X measured here: the prefill takes 790 us cold and 520 us warm), so
+# every timed region is preceded by at least this much back-to-back work on
+# top of the requested warm-up steps.
+CLOCK_WARM_MS = 60.0
+
+
+def warm_clocks(fn, ms=CLOCK_WARM_MS):
+    """Run fn back to back until at least ``ms`` of device time has passed."""
     import torch
 
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        if n in (1, 2, 4) or n % 8 == 0:
+            stop.record()
+            stop.synchronize()
+            if start.elapsed_time(stop) >= ms:
+                return n
+
+
+def time_steps(fn, steps, warmup):
+    """Average ms per call of fn over `steps` timed calls (after a clock
+    warm-up of at least CLOCK_WARM_MS and `warmup` further calls)."""
+    import torch
+
+    warm_clocks(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -187,10 +214,7 @@ def bench_decode_sweep(steps, warmup):
             def step():
                 plx_decode(q, rho, kc, vc, cl, num_splits=0, workspace=ws, o=o, lse=False)
 
-            # warm up for >= 50 ms whatever the cell's size: the clocks ramp
-            # only under sustained work
-            est = time_steps(step, 5, 2)
-            ms = time_steps(step, steps, max(warmup, int(50.0 / max(est, 1e-3))))
+            ms = time_steps(step, steps, warmup)
             nbytes = B * Hkv * ctx * d * 2 * 2 + B * Hq * d * (2 + 2 + 4)
             gbs = nbytes / (ms * 1e-3) / 1e9
             cells.append({"B": B, "ctx": ctx, "us_per_step": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
@@ -233,7 +257,7 @@ def bench_train(steps, warmup):
     out = {"workload": f"bf16 training step fwd+bwd B={B} Hq={Hq} Hkv={Hkv} T={T} d={d}",
            "fwd_ms": ms_f, "bwd_ms": ms_b, "step_ms": ms_f + ms_b,
            "fwd_tflops": fl_f / (ms_f * 1e-3) / 1e12, "bwd_tflops": fl_b / (ms_b * 1e-3) / 1e12,
-           "step_tflops": (fl_f + fl_b) / ((ms_f + ms_b) * 1e-3) / 1e12}
+           "step_tflops": (fl_f + fl_b) / ((ms_f + ms_b) * 1e-3) / 1e12, "bwd_flops": fl_b}
     out["bwd_mfma_frac"] = out["bwd_tflops"] / PEAK_BF16_TFLOPS
     del q, k, v, rho, d_o, fwd, grads
     torch.cuda.empty_cache()
@@ -396,6 +420,8 @@ TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "prefill": ["plx_fwd.hip", "plx_common.hpp"],
     "decode": ["plx_decode.hip", "plx_common.hpp"],
+    "decode_long": ["plx_decode.hip", "plx_common.hpp"],
+    "bwd": ["plx_bwd.hip", "plx_common.hpp"],
     "proj": ["plx_proj.hip", "plx_common.hpp"],
 }
 
@@ -459,15 +485,38 @@ def cpu_baseline(budget_s=12.0):
         flops += 4 * 2 * d * (i + 1)
         n_rows += 1
     dt = time.perf_counter() - t0
+    blas, threads = "unknown", 1
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            threads = max(p.get("num_threads", 1) for p in pools)
+            blas = ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in pools)
     except Exception:  # pragma: no cover
-        threads = 1
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    cpu_model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu_model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    # the oracle's cost per row is proportional to its key count i + 1, and
+    # the rows were drawn uniformly, so the whole workload (B=4, Hq=16 rows
+    # of every length 1..4096) scales linearly from the sample
+    whole_units = 4 * 16 * T * (T + 1) // 2
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n_rows} random rows (uniform i in [0,4096)) of the B=4 Hq=16 T=4096 d=128 "
-                      f"prefill, fp64 numpy with explicit covariance per row, {dt:.1f} s"}
+                      f"prefill, fp64 numpy with explicit covariance per row, {dt:.1f} s",
+            "affinity_cores": int(affinity), "cpu_model": cpu_model, "blas": blas,
+            "seconds_sampled": round(dt, 2),
+            "seconds_whole_workload_extrapolated": round(dt * whole_units / (flops / (8 * d)), 1)}
 
 
 def main():
@@ -580,11 +629,19 @@ def main():
                 line[key]["roofline"] = {
                     "bound": "hbm", "achieved": round(r["GB/s"], 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(r["GB/s"] / PEAK_HBM_GBS, 4),
-                    "traffic": measured_traffic("decode") if key == "decode" else None,
+                    "traffic": measured_traffic(key),
                     "kernel": "decode16_balanced_kernel<128,2> + decode_merge_balanced_kernel<128>",
                     **({"measured_peak": peaks["hbm_read_gbs"],
                         "frac_of_measured": round(r["GB/s"] / peaks["hbm_read_gbs"], 4)} if peaks else {}),
                     "algorithmic_bytes_per_launch": r["bytes"]}
+    if "train" in res:
+        r = res["train"]
+        line["train"]["roofline"] = {
+            "bound": "mfma", "achieved": round(r["bwd_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(r["bwd_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic("bwd"), "kernel": "plx_bwd (all of its kernels)",
+            "algorithmic_flops_per_launch": r["bwd_flops"]}
+    line["clock_warmup_ms"] = CLOCK_WARM_MS
     if peaks:
         line["measured_peaks"] = peaks
     if not args.no_cpu and args.only in ("all", "prefill"):

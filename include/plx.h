@@ -32,6 +32,11 @@
  *     well in plx_bwd) must lie within fp16's range, |x| <= 65504: the
  *     conversion is exact down to 2^-14 and rounds smaller magnitudes to fp16's
  *     subnormal grid (absolute error <= 2^-25); larger ones become infinite.
+ *   - bf16 probe scores: the forward and decode kernels round p * r (p <= 16,
+ *     the softmax numerator against a running maximum that moves only when a
+ *     score exceeds it by more than 4 in log2 units) to fp16, so every probe
+ *     score must satisfy |r_ij| = |rho_i . k_j| <= 4094 (fp16's largest
+ *     value over 16).  The workloads' probes give |r| of a few tens.
  *   - Supported head dims: d = 64 or 128 (d_k = d_v = d) everywhere; d = 256 as
  *     well for bf16 in plx_fwd_prefill(_ex), plx_decode(_ex) and plx_qkvr_proj
  *     (PLX_ERR_UNSUPPORTED for fp32 and for plx_bwd).
@@ -103,6 +108,14 @@ plx_status plx_fwd_prefill(const void* q, const void* k, const void* v, const vo
 
 /*
  * Decode: one new query and probe per (b, h) against a KV cache.
+ *
+ * The pages describe a custom decode kernel that streams the KV cache once
+ * for both branches ("Riepilogo Tecnico: Parallax ..." (gist.science),
+ * section "Algoritmo Consapevole dell'Hardware") and a variant tuned for
+ * parallel decoding ("Внимание нового поколения ..." (denisavetisyan.com),
+ * the decode-latency figure); the key split below is that parallelism.  The
+ * output is the operator above at the query's position, with the cache rows
+ * as its key set.
  *
  * Query (b, h) attends to the cache rows [0, ctx_len[b]) of KV head h/(Hq/Hkv)
  * (the cache already holds the current token; no mask).  The keys are cut into
@@ -213,8 +226,11 @@ plx_status plx_qkvr_proj(const void* x, const void* w, void* q, void* k, void* v
                          plx_stream stream);
 
 /*
- * Backward of the causal prefill (the pages give none; these are the exact
- * gradients of the forward above with rho an independent input).
+ * Backward of the causal prefill.  The pages give no backward pass; this is
+ * the exact gradient of the operator defined by "当注意力学会追问..."
+ * (zhichai.net), section 1.3, and "Riepilogo Tecnico: Parallax ..."
+ * (gist.science), section "Meccanismo Principale" (o = o^SA - Sigma_KV rho,
+ * eta = 0), with rho an independent input, written out in closed form:
  *
  * With g = dO_i, A_ij = g . v_j, G_i = g . o_i, delta_i = g . vbar_i,
  * c_i = kbar_i . rho_i, r_ij = rho_i . k_j and w_ij recomputed from the saved LSE:

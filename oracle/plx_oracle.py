@@ -72,6 +72,8 @@ __all__ = [
     "row_backward",
     "prefill_backward",
     "prefill_backward_kv_rows",
+    "prefill_backward_rows",
+    "prefill_backward_group",
     "uniform_weights",
     "row_family",
     "correction_to_output",
@@ -261,6 +263,85 @@ def prefill_backward_kv_rows(get_row, keys, T, Hq, Hkv, scale):
         dks.append(acc_k)
         dvs.append(acc_v)
     return np.array(dks), np.array(dvs)
+
+
+def prefill_backward_rows(get_row, rows, Hq, Hkv, scale):
+    """dQ and drho of sampled query rows (b, h, i).  ``get_row(b, h, hk, i)``
+    returns (q_i, K[:i+1], V[:i+1], rho_i, g_i) as float64.  Returns (dq, drho)
+    stacked in row order."""
+    dqs, drs = [], []
+    for b, h, i in rows:
+        qi, K, V, ri, gi = get_row(b, h, _kv_head(h, Hq, Hkv), i)
+        dq, _, _, dr = row_backward(qi, K, V, ri, gi, scale)
+        dqs.append(dq)
+        drs.append(dr)
+    return np.array(dqs), np.array(drs)
+
+
+def prefill_backward_group(q, k, v, rho, g, scale, magnitudes=False, rows_per_step=256):
+    """Whole-group backward in closed form, on dense causal matrices.
+
+    One KV head and the G query heads that share it: q, rho, g [G, T, d];
+    k, v [T, d] (float64).  This is the second form of the backward, for
+    sizes where ``row_backward``'s explicit d x d covariance per row is too
+    slow (a full T = 4096 group).  It writes the gradient of <g, o> out
+    directly from o_i = sum_j w_ij (1 + c_i - r_ij) v_j (the same o as
+    ``row_from_weights``: vbar - Sigma rho expanded against rho):
+        A_ij = g_i . v_j,  G_i = g_i . o_i,  delta_i = g_i . vbar_i,
+        dV_j  = sum_i w_ij (1 + c_i - r_ij) g_i,
+        dS_ij = w_ij [(1 + c_i - r_ij) A_ij - G_i + delta_i (r_ij - c_i)],
+        dR_ij = -w_ij (A_ij - delta_i),
+        dQ = tau dS K,  dK = tau dS^T Q + dR^T rho,  drho = dR K,
+    with dK and dV summed over the G heads.  Query rows are taken
+    ``rows_per_step`` at a time (each row against its causal keys, masked
+    to j <= i); the CPU tests pin the result to ``prefill_backward``
+    (reverse mode through the explicit covariance).
+
+    Returns dict(dq, drho [G, T, d], dk, dv [T, d]).  With ``magnitudes`` it
+    also returns, per gradient element, the sum of the absolute values of
+    the products that make it up (``m_dq`` ...), each factor replaced by a
+    bound on its own magnitude (|1 + c - r| by 1 + |c| + |r|, and so on): the
+    scale against which a floating-point evaluation's rounding is measured.
+    """
+    G, T, d = q.shape
+    out = {"dq": np.zeros((G, T, d)), "drho": np.zeros((G, T, d)),
+           "dk": np.zeros((T, d)), "dv": np.zeros((T, d))}
+    if magnitudes:
+        for n in ("m_dq", "m_drho", "m_dk", "m_dv"):
+            out[n] = np.zeros_like(out[n[2:]])
+    for h in range(G):
+        for i0 in range(0, T, rows_per_step):
+            i1 = min(T, i0 + rows_per_step)
+            K, V = k[:i1], v[:i1]  # every key some row of the step sees
+            qh, rh, gh = q[h, i0:i1], rho[h, i0:i1], g[h, i0:i1]
+            causal = np.arange(i1)[None, :] <= np.arange(i0, i1)[:, None]
+            s = np.where(causal, scale * (qh @ K.T), -np.inf)
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            w = e / e.sum(axis=1, keepdims=True)
+            r = rh @ K.T
+            a = gh @ V.T
+            c = np.sum(w * r, axis=1)
+            vbar = w @ V
+            o = vbar * (1.0 + c)[:, None] - (w * r) @ V
+            Gi = np.sum(gh * o, axis=1)
+            dl = np.sum(gh * vbar, axis=1)
+            f = 1.0 + c[:, None] - r
+            ds = w * (f * a - Gi[:, None] + dl[:, None] * (r - c[:, None]))
+            dr = -w * (a - dl[:, None])
+            out["dq"][h, i0:i1] = scale * (ds @ K)
+            out["drho"][h, i0:i1] = dr @ K
+            out["dk"][:i1] += scale * (ds.T @ qh) + dr.T @ rh
+            out["dv"][:i1] += (w * f).T @ gh
+            if magnitudes:
+                fa = 1.0 + np.abs(c)[:, None] + np.abs(r)
+                dsa = w * (fa * np.abs(a) + np.abs(Gi)[:, None]
+                           + np.abs(dl)[:, None] * (np.abs(r) + np.abs(c)[:, None]))
+                dra = w * (np.abs(a) + np.abs(dl)[:, None])
+                out["m_dq"][h, i0:i1] = scale * (dsa @ np.abs(K))
+                out["m_drho"][h, i0:i1] = dra @ np.abs(K)
+                out["m_dk"][:i1] += scale * (dsa.T @ np.abs(qh)) + dra.T @ np.abs(rh)
+                out["m_dv"][:i1] += (w * fa).T @ np.abs(gh)
+    return out
 
 
 # -- family corners and the correction-to-output ratio -------------------------

@@ -114,10 +114,25 @@ def _need(t, name, shape, dtype, device):
         raise ValueError(f"{name}: shape {tuple(t.shape)} != expected {tuple(shape)}")
     if t.dtype != dtype:
         raise ValueError(f"{name}: dtype {t.dtype} != {dtype}")
-    if t.device != device:
-        raise ValueError(f"{name}: on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+def _need_workspace(ws, device, need):
+    """A caller-supplied workspace: device memory of at least ``need`` bytes."""
+    if ws.device != device:
+        raise ValueError(f"workspace: on {ws.device}, expected {device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace: must be contiguous")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace: {ws.numel() * ws.element_size()} bytes < {need} needed")
+
+
+def _need_gpu(device):
+    if device.type != "cuda":
+        raise ValueError(f"tensors are on {device}; the HIP library takes GPU tensors only")
 
 
 def plx_fwd_prefill(q, k, v, rho, scale=None, *, o=None, lse=True, aux=False):
@@ -145,6 +160,9 @@ def _prefill(q, k, v, rho, scale, *, o, lse, aux, ex):
     for name, t, shp in (("q", q, (B, Hq, T, d)), ("k", k, (B, Hkv, T, d)),
                          ("v", v, (B, Hkv, T, d)), ("rho", rho, (B, Hq, T, d))):
         _need(t, name, shp, q.dtype, dev)
+    if o is not None:
+        _need(o, "o", (B, Hq, T, d), torch.float32, dev)
+    _need_gpu(dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if o is None:
@@ -196,18 +214,27 @@ def plx_decode_ex(q, rho, k_cache, v_cache, ctx_len, scale=None, *, flags=0, cor
 
 def _decode(q, rho, k_cache, v_cache, ctx_len, scale, *, num_splits, workspace, o, lse, ex):
     torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError(f"q must be [B, Hq, d] and the caches [B, Hkv, S_max, d]; got "
+                         f"{tuple(q.shape)} and {tuple(k_cache.shape)}")
     B, Hq, d = q.shape
     Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
     dev = q.device
+    _need(q, "q", (B, Hq, d), q.dtype, dev)
     _need(rho, "rho", (B, Hq, d), q.dtype, dev)
     _need(k_cache, "k_cache", (B, Hkv, S_max, d), q.dtype, dev)
     _need(v_cache, "v_cache", (B, Hkv, S_max, d), q.dtype, dev)
     _need(ctx_len, "ctx_len", (B,), torch.int32, dev)
+    if o is not None:
+        _need(o, "o", (B, Hq, d), torch.float32, dev)
+    _need_gpu(dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = decode_workspace_size(B, Hq, Hkv, S_max, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    else:
+        _need_workspace(workspace, dev, need)
     if o is None:
         o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     lse_t = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse else None
@@ -241,6 +268,7 @@ def plx_qkvr_proj(x, w, Hq, Hkv, d, *, out=None):
     B, T, D = x.shape
     dev = x.device
     N = (2 * Hq + 2 * Hkv) * d
+    _need(x, "x", (B, T, D), x.dtype, dev)
     _need(w, "w", (N, D), x.dtype, dev)
     if out is None:
         out = {
@@ -251,7 +279,7 @@ def plx_qkvr_proj(x, w, Hq, Hkv, d, *, out=None):
         }
     for n, H in (("q", Hq), ("k", Hkv), ("v", Hkv), ("rho", Hq)):
         _need(out[n], n, (B, H, T, d), x.dtype, dev)
-    _need(x, "x", (B, T, D), x.dtype, dev)
+    _need_gpu(dev)
     st = lib().plx_qkvr_proj(_ptr(x), _ptr(w), _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]),
                              _ptr(out["rho"]), B, T, D, Hq, Hkv, d, _dtype_code(x), _stream(dev))
     _check(st, "plx_qkvr_proj")
@@ -268,17 +296,26 @@ def plx_bwd(q, k, v, rho, d_o, o, lse, c, vbar, scale=None, *, workspace=None, g
     B, Hq, T, d = q.shape
     Hkv = k.shape[1]
     dev = q.device
-    for name, t, shp in (("k", k, (B, Hkv, T, d)), ("v", v, (B, Hkv, T, d)),
+    for name, t, shp in (("q", q, (B, Hq, T, d)), ("k", k, (B, Hkv, T, d)), ("v", v, (B, Hkv, T, d)),
                          ("rho", rho, (B, Hq, T, d)), ("d_o", d_o, (B, Hq, T, d))):
         _need(t, name, shp, q.dtype, dev)
     for name, t, shp in (("o", o, (B, Hq, T, d)), ("lse", lse, (B, Hq, T)), ("c", c, (B, Hq, T)),
                          ("vbar", vbar, (B, Hq, T, d))):
         _need(t, name, shp, torch.float32, dev)
+    if grads is not None:
+        for name, shp in (("dq", (B, Hq, T, d)), ("dk", (B, Hkv, T, d)), ("dv", (B, Hkv, T, d)),
+                          ("drho", (B, Hq, T, d))):
+            if name not in grads:
+                raise ValueError(f"grads: missing {name}")
+            _need(grads[name], name, shp, torch.float32, dev)
+    _need_gpu(dev)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = bwd_workspace_size(B, Hq, Hkv, T, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    else:
+        _need_workspace(workspace, dev, need)
     if grads is None:
         grads = {
             "dq": torch.empty((B, Hq, T, d), dtype=torch.float32, device=dev),

@@ -247,3 +247,64 @@ def _proj(**kw):
 ])
 def test_proj_validation(kw, status):
     assert _proj(**kw) == status
+
+
+# -- the Python binding rejects malformed tensors before any library call -----
+
+def _bf16(*shape):
+    import torch
+
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+def test_binding_rejects_noncontiguous_decode_query():
+    """The last-token slice q[:, :, -1, :] of a [B, H, T, d] tensor is not
+    contiguous; the binding must refuse it rather than read it with the wrong
+    strides."""
+    import torch
+
+    from parallax_local_linear_plx_amd import plx_decode
+
+    B, Hq, Hkv, S, d = 2, 4, 2, 16, 64
+    q = _bf16(B, Hq, 5, d)[:, :, -1, :]
+    assert not q.is_contiguous()
+    with pytest.raises(ValueError, match="contiguous"):
+        plx_decode(q, _bf16(B, Hq, d), _bf16(B, Hkv, S, d), _bf16(B, Hkv, S, d),
+                   torch.full((B,), S, dtype=torch.int32))
+
+
+def test_binding_rejects_wrong_output_buffers():
+    import torch
+
+    from parallax_local_linear_plx_amd import plx_bwd, plx_decode, plx_fwd_prefill
+
+    B, Hq, Hkv, T, d = 1, 2, 1, 8, 64
+    q, k = _bf16(B, Hq, T, d), _bf16(B, Hkv, T, d)
+    with pytest.raises(ValueError, match="dtype"):
+        plx_fwd_prefill(q, k, k, q, o=torch.zeros(B, Hq, T, d, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="shape"):
+        plx_fwd_prefill(q, k, k, q, o=torch.zeros(B, Hq, T + 1, d))
+    with pytest.raises(ValueError, match="dtype"):
+        plx_decode(_bf16(B, Hq, d), _bf16(B, Hq, d), k, k, torch.full((B,), T, dtype=torch.int32),
+                   o=torch.zeros(B, Hq, d, dtype=torch.float16))
+    f32 = lambda *s: torch.zeros(*s)  # noqa: E731
+    grads = {"dq": f32(B, Hq, T, d), "dk": f32(B, Hkv, T, d), "dv": f32(B, Hkv, T, d),
+             "drho": f32(B, Hq, T + 1, d)}
+    with pytest.raises(ValueError, match="shape"):
+        plx_bwd(q, k, k, q, q, f32(B, Hq, T, d), f32(B, Hq, T), f32(B, Hq, T), f32(B, Hq, T, d),
+                grads=grads)
+    with pytest.raises(ValueError, match="contiguous"):
+        plx_bwd(q.transpose(2, 3).contiguous().transpose(2, 3), k, k, q, q, f32(B, Hq, T, d),
+                f32(B, Hq, T), f32(B, Hq, T), f32(B, Hq, T, d))
+
+
+def test_binding_refuses_host_tensors():
+    """Host tensors would hand the kernels host pointers."""
+    import torch
+
+    from parallax_local_linear_plx_amd import plx_fwd_prefill
+
+    q, k = _bf16(1, 2, 8, 64), _bf16(1, 1, 8, 64)
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        plx_fwd_prefill(q, k, k, q)
+    assert torch.zeros(1).device.type == "cpu"

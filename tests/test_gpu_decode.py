@@ -5,6 +5,7 @@ import pytest
 
 from oracle import plx_oracle as orc
 from parallax_local_linear_plx_amd import inputs
+from tests import _fetch
 from tests._util import LSE_ABS, check_bf16, check_fp32, say, to_device
 
 pytestmark = pytest.mark.gpu
@@ -34,14 +35,7 @@ def _run(wl, num_splits=0, t=None):
 
 
 def _oracle(wl, heads=None):
-    q = wl.tensors["q"].f64().reshape(wl.B, wl.Hq, wl.d)
-    rho = wl.tensors["rho"].f64().reshape(wl.B, wl.Hq, wl.d)
-
-    def fetch(b, hk, n):
-        return (wl.tensors["k"].f64_slice((b, hk, slice(0, n))),
-                wl.tensors["v"].f64_slice((b, hk, slice(0, n))))
-
-    return orc.decode_forward(q, rho, fetch, wl.Hkv, wl.ctx_len, wl.scale, heads=heads)
+    return _fetch.decode_oracle(wl, heads)
 
 
 @pytest.mark.parametrize("num_splits", [0, 1, 3, 7])

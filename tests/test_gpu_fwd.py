@@ -5,6 +5,7 @@ import pytest
 
 from oracle import plx_oracle as orc
 from parallax_local_linear_plx_amd import inputs
+from tests import _fetch
 from tests._util import LSE_ABS, check_bf16, check_fp32, say, to_device
 
 pytestmark = pytest.mark.gpu
@@ -109,12 +110,7 @@ def test_bf16_prefill_full_size_sampled_rows(gpu_lib):
     rows = [(0, 0, 0), (0, 0, 1), (3, 15, 4095), (1, 7, 4094), (2, 8, 2048), (0, 1, 127), (0, 1, 128)]
     rows += [(int(g.integers(4)), int(g.integers(16)), int(g.integers(4096))) for _ in range(40)]
     T = wl.T
-
-    def get_row(b, h, hk, i):
-        return (wl.tensors["q"].f64_slice((b, h, i)), wl.tensors["k"].f64_slice((b, hk, slice(0, i + 1))),
-                wl.tensors["v"].f64_slice((b, hk, slice(0, i + 1))), wl.tensors["rho"].f64_slice((b, h, i)))
-
-    ref_o, ref_lse = orc.prefill_rows(get_row, rows, wl.Hq, wl.Hkv, wl.scale)
+    ref_o, ref_lse = _fetch.prefill_oracle_rows(wl, rows)
     got_o = np.array([got["o"][b, h, i] for b, h, i in rows])
     got_lse = np.array([got["lse"][b, h, i] for b, h, i in rows])
     check_bf16(got_o, ref_o, "o (sampled rows)")
