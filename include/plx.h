@@ -248,8 +248,8 @@ plx_status plx_qkvr_proj(const void* x, const void* w, void* q, void* k, void* v
  *   dk, dv      [B, Hkv, T, d] fp32, written (overwritten, not accumulated)
  *   workspace   at least plx_bwd_workspace_size(...) bytes, 16-byte aligned:
  *               G_i = dO_i . o_i and delta_i (fp32 per query row), then, used by
- *               the bf16 path, fp16 copies of q, rho, dO, k and v (one
- *               conversion pass, so that the main kernels read fp16 operands)
+ *               the bf16 path, fp16 copies of q, rho, dO ([B, Hq, T, d]) and
+ *               k ([B, Hkv, T, d]) that the kernels stage as MFMA operands
  * The result is deterministic (no atomics): one kernel owns each key block and
  * one kernel owns each query block.
  */

@@ -122,7 +122,8 @@ def _kv_head(h, Hq, Hkv):
 def prefill_forward(q, k, v, rho, scale):
     """Causal prefill.  q, rho: [B, Hq, T, d]; k, v: [B, Hkv, T, d] (float64).
 
-    Returns dict(o, o_sa, lse) with o, o_sa [B, Hq, T, d_v] and lse [B, Hq, T].
+    Returns dict(o, o_sa, lse, c) with o, o_sa [B, Hq, T, d_v], lse [B, Hq, T]
+    and c = kbar_i . rho_i [B, Hq, T] (the probe's projection on the mean key).
     """
     B, Hq, T, _ = q.shape
     Hkv = k.shape[1]
@@ -130,13 +131,16 @@ def prefill_forward(q, k, v, rho, scale):
     o = np.empty((B, Hq, T, dv))
     o_sa = np.empty((B, Hq, T, dv))
     lse = np.empty((B, Hq, T))
+    c = np.empty((B, Hq, T))
     for b in range(B):
         for h in range(Hq):
             hk = _kv_head(h, Hq, Hkv)
             for i in range(T):
-                o[b, h, i], o_sa[b, h, i], lse[b, h, i], _ = row_forward(
-                    q[b, h, i], k[b, hk, : i + 1], v[b, hk, : i + 1], rho[b, h, i], scale)
-    return {"o": o, "o_sa": o_sa, "lse": lse}
+                K, V = k[b, hk, : i + 1], v[b, hk, : i + 1]
+                w, lse[b, h, i] = softmax_weights(scale * (K @ q[b, h, i]))
+                o[b, h, i], o_sa[b, h, i], kbar, _ = row_from_weights(w, K, V, rho[b, h, i])
+                c[b, h, i] = kbar @ rho[b, h, i]
+    return {"o": o, "o_sa": o_sa, "lse": lse, "c": c}
 
 
 def prefill_rows(get_row, rows, Hq, Hkv, scale):

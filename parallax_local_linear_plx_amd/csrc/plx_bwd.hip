@@ -11,11 +11,13 @@
 //   dQ = tau dS K,  dK = tau dS^T Q + dR^T rho,  drho = dR K.
 //
 // Kernels, no atomics (the result is deterministic):
-//   pre   : G and delta per row.
-//   cvt   : (bf16 inputs) fp16 copies of q, rho, dO, k and v in the workspace.
+//   pre   : (fp32 inputs) G and delta per row.
+//   cvt   : (bf16 inputs) an fp16 copy of k in the workspace.
 //   dq    : query-outer, laid out like the forward (S^T = K Q^T, one query per
 //           lane column): recomputes S, R and A^T = V dO^T per key tile, forms
 //           dS, dR in registers and accumulates dQ^T = K^T dS^T, drho^T = K^T dR^T.
+//           The bf16 kernel also forms G and delta of its rows and writes fp16
+//           copies of q, rho and dO for the key-outer kernel.
 //   dkdv  : key-outer: one key per lane column (S = Q K^T), loops over the
 //           query tiles of every head that shares the KV head, accumulates
 //           dV^T = dO^T Ptilde and dK^T = Q^T (tau dS) + rho^T dR.
@@ -414,41 +416,46 @@ __device__ __forceinline__ f16x8 cvt_bf16x8_f16(u32x4 raw) {
   return h;
 }
 
-// bf16 -> fp16 copy of n8 chunks of 8 elements: the bf16 backward reads its
-// MFMA operands (q, rho, dO, K, V) from these copies, so the main kernels stage
-// tiles without converting them again for every workgroup that reads them.
+// bf16 -> fp16 copy of n8 chunks of 8 elements: the dQ kernel stages its K
+// tiles from this copy, so a tile read by every query block of a head is not
+// converted again by each of them.
 __global__ __launch_bounds__(256) void cvt_f16_kernel(const u32x4* __restrict__ src, f16x8* __restrict__ dst,
                                                      long long n8) {
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long long)gridDim.x * 256)
     dst[i] = cvt_bf16x8_f16(src[i]);
 }
 
-// dQ and drho on 16x16x32 MFMA tiles, two waves per SIMD (bf16 inputs, read
-// from their fp16 copies).  The layout follows the forward kernel: a wave owns
-// 16 query rows (lane column c = lane % 16; the four 16-lane groups g split the
-// keys of a score tile and the head dimension of the gradient tiles).  Per
-// 32-key sub-tile:
-//   S^T, R^T = K [Q; rho]^T and A^T = V dO^T (32 keys x 16 queries), A = K / V
-//     rows from LDS, B = Q / rho / dO from registers;
+// dQ and drho on 16x16x32 MFMA tiles, two waves per SIMD (bf16 inputs).  The
+// layout follows the forward kernel: a wave owns 16 query rows (lane column
+// c = lane % 16; the four 16-lane groups g split the keys of a score tile and
+// the head dimension of the gradient tiles).  Per 32-key sub-tile:
+//   S^T, R^T = K [Q; rho]^T (fp16 MFMAs: K from its fp16 copy, Q and rho
+//     converted in registers) and A^T = V dO^T (bf16 MFMAs on the inputs as
+//     stored), 32 keys x 16 queries, A = K / V rows from LDS, B from registers;
 //   dS^T, dR^T in registers, rounded to the fp16 B operand of
 //   [dQ | drho]^T += K^T [dS | dR]^T, A = K^T from transpose reads of the K tile.
 // Workgroup: 8 waves, 128 query rows of one (b, h); 128-key K / V tiles
 // double-buffered in LDS, one barrier per tile.
+// The kernel also does the per-row preprocessing the key-outer kernel needs,
+// for the rows it owns: G_i = dO_i . o_i, delta_i = dO_i . vbar_i, and fp16
+// copies of q_i, rho_i and dO_i (the key-outer kernel's LDS tiles), so no
+// separate pass reads dO, o and vbar.
 constexpr int DQB_BC = 128;
 template <int D>
 struct DqbSmem {
   static constexpr int LD = D + 16;  // as the forward's tiles: conflict-free rows and transpose reads
   alignas(16) _Float16 k[2][DQB_BC * LD];
-  alignas(16) _Float16 v[2][DQB_BC * LD];
+  alignas(16) uint16_t v[2][DQB_BC * LD];  // bf16, as stored
 };
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dq16b_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ rho, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
-    const float* __restrict__ c_aux, const float* __restrict__ Gv, const float* __restrict__ dlt,
-    float* __restrict__ dq, float* __restrict__ drho, int B, int Hq, int Hkv, int T, float scale,
-    float scale_log2) {
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k16, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ rho, const uint16_t* __restrict__ d_o, const float* __restrict__ o,
+    const float* __restrict__ vbar, const float* __restrict__ lse, const float* __restrict__ c_aux,
+    float* __restrict__ Gv, float* __restrict__ dlt, _Float16* __restrict__ q16,
+    _Float16* __restrict__ r16, _Float16* __restrict__ g16, float* __restrict__ dq,
+    float* __restrict__ drho, int B, int Hq, int Hkv, int T, float scale, float scale_log2) {
   constexpr int NW = 8, NT = 64 * NW, BR = 16 * NW;
   constexpr int NS = D / 32, ND = D / 16, CPR = D / 8;
   constexpr int NCH = DQB_BC * CPR / NT;  // 16-byte chunks per thread per tile and tensor
@@ -471,7 +478,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16b_kernel(
   const bool qvalid = my_q < T;
 
   const size_t rowbase = (size_t)bh * T;
-  const uint16_t* kp = k + ((size_t)(b * Hkv + hk) * T) * D;
+  const uint16_t* kp = k16 + ((size_t)(b * Hkv + hk) * T) * D;
   const uint16_t* vp = v + ((size_t)(b * Hkv + hk) * T) * D;
   const int kend = min(T, q0 + BR);
   const int ntiles = (kend + DQB_BC - 1) / DQB_BC;
@@ -500,7 +507,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16b_kernel(
   };
 
   gload(0);
-  f16x8 qop[NS], rop[NS], gop[NS];
+  // this lane's quarter of its query row: elements 32 s + 8 g .. + 8
+  f16x8 qop[NS], rop[NS];
+  bf16x8 gop[NS];
+  float Gi = 0.f, di = 0.f;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     u32x4 qa = {0u, 0u, 0u, 0u}, ra = qa, ga = qa;
@@ -509,15 +519,39 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16b_kernel(
       qa = *reinterpret_cast<const u32x4*>(q + off);
       ra = *reinterpret_cast<const u32x4*>(rho + off);
       ga = *reinterpret_cast<const u32x4*>(d_o + off);
+      const f32x4 o0 = *reinterpret_cast<const f32x4*>(o + off);
+      const f32x4 o1 = *reinterpret_cast<const f32x4*>(o + off + 4);
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(vbar + off);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(vbar + off + 4);
+      const u16x8 gb = __builtin_bit_cast(u16x8, ga);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = bf16_bits_to_f32(gb[e]), x1 = bf16_bits_to_f32(gb[4 + e]);
+        Gi = __builtin_fmaf(x0, o0[e], __builtin_fmaf(x1, o1[e], Gi));
+        di = __builtin_fmaf(x0, v0[e], __builtin_fmaf(x1, v1[e], di));
+      }
     }
-    qop[s] = __builtin_bit_cast(f16x8, qa);
-    rop[s] = __builtin_bit_cast(f16x8, ra);
-    gop[s] = __builtin_bit_cast(f16x8, ga);
+    qop[s] = cvt_bf16x8_f16(qa);
+    rop[s] = cvt_bf16x8_f16(ra);
+    gop[s] = __builtin_bit_cast(bf16x8, ga);
+    if (qvalid) {
+      const size_t off = (rowbase + my_q) * D + 32 * s + 8 * g;
+      *reinterpret_cast<f16x8*>(q16 + off) = qop[s];
+      *reinterpret_cast<f16x8*>(r16 + off) = rop[s];
+      *reinterpret_cast<f16x8*>(g16 + off) = cvt_bf16x8_f16(ga);
+    }
+  }
+  // the four 16-lane groups hold disjoint quarters of the row
+  Gi += __shfl_xor(Gi, 16, 64);
+  Gi += __shfl_xor(Gi, 32, 64);
+  di += __shfl_xor(di, 16, 64);
+  di += __shfl_xor(di, 32, 64);
+  if (qvalid && g == 0) {
+    Gv[rowbase + my_q] = Gi;
+    dlt[rowbase + my_q] = di;
   }
   const float lse2 = qvalid ? lse[rowbase + my_q] * kLog2e : 0.f;
   const float ci = qvalid ? c_aux[rowbase + my_q] : 0.f;
-  const float Gi = qvalid ? Gv[rowbase + my_q] : 0.f;
-  const float di = qvalid ? dlt[rowbase + my_q] : 0.f;
   // dS = p [A k1 + r (delta - A) - k2] with k1 = 1 + c, k2 = G + delta c
   const float k1 = 1.f + ci, k2 = Gi + di * ci;
   lds_put(0);
@@ -535,13 +569,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16b_kernel(
     unsigned kaddr = lds_addr(&sm.k[buf][(32 * st + c) * SM::LD + 8 * g]);
     unsigned vaddr = lds_addr(&sm.v[buf][(32 * st + c) * SM::LD + 8 * g]);
     asm volatile("" : "+v"(kaddr), "+v"(vaddr));
-    f16x8 ka[2][NS], va[2][NS];
+    f16x8 ka[2][NS];
+    bf16x8 va[2][NS];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         ka[t][s] = __builtin_bit_cast(f16x8, ld128_at(kaddr + 2 * (16 * t * SM::LD + 32 * s)));
-        va[t][s] = __builtin_bit_cast(f16x8, ld128_at(vaddr + 2 * (16 * t * SM::LD + 32 * s)));
+        va[t][s] = __builtin_bit_cast(bf16x8, ld128_at(vaddr + 2 * (16 * t * SM::LD + 32 * s)));
       }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
@@ -553,7 +588,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16b_kernel(
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[t][s], qop[s], s == 0 ? z : sacc[t], 0, 0, 0);
         racc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[t][s], rop[s], s == 0 ? z : racc[t], 0, 0, 0);
-        aacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[t][s], gop[s], s == 0 ? z : aacc[t], 0, 0, 0);
+        aacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[t][s], gop[s], s == 0 ? z : aacc[t], 0, 0, 0);
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -732,8 +767,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16b_kernel(
       ka = *reinterpret_cast<const u32x4*>(k + off);
       va = *reinterpret_cast<const u32x4*>(v + off);
     }
-    kop[s] = __builtin_bit_cast(f16x8, ka);
-    vop[s] = __builtin_bit_cast(f16x8, va);
+    kop[s] = cvt_bf16x8_f16(ka);  // K and V as stored (bf16), converted once here
+    vop[s] = cvt_bf16x8_f16(va);
   }
   lds_put(0);
   __syncthreads();
@@ -868,41 +903,39 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   const long long rows = (long long)B * Hq * T;
   float* G = ws;
   float* dl = ws + rows;
-  hipLaunchKernelGGL((bwd_pre_kernel<Pol, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
-                     stream, (const in_t*)d_o, o, vbar, G, dl, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
   const int nqb = (T + DQ_BR - 1) / DQ_BR;
   const int nkb = (T + KV_BK - 1) / KV_BK;
   if constexpr (sizeof(in_t) == 2) {
-    // fp16 copies of the five inputs follow G and delta in the workspace
+    // workspace after G and delta: fp16 copies of q, rho, dO (written by the
+    // dQ kernel) and of K (written by the conversion pass)
     const size_t nq = (size_t)rows * D, nk = (size_t)B * Hkv * T * D;
-    uint16_t* h = (uint16_t*)((char*)ws + bwd_ws_align(2 * rows * sizeof(float)));
-    uint16_t* q16 = h;
-    uint16_t* r16 = q16 + nq;
-    uint16_t* g16 = r16 + nq;
-    uint16_t* k16 = g16 + nq;
-    uint16_t* v16 = k16 + nk;
-    const void* src[5] = {q, rho, d_o, k, v};
-    uint16_t* dst[5] = {q16, r16, g16, k16, v16};
-    for (int i = 0; i < 5; ++i) {
-      const long long n8 = (long long)(i < 3 ? nq : nk) / 8;
+    _Float16* q16 = (_Float16*)((char*)ws + bwd_ws_align(2 * rows * sizeof(float)));
+    _Float16* r16 = q16 + nq;
+    _Float16* g16 = r16 + nq;
+    _Float16* k16 = g16 + nq;
+    {
+      const long long n8 = (long long)nk / 8;
       const unsigned blocks = (unsigned)std::min<long long>((n8 + 255) / 256, 8192);
-      hipLaunchKernelGGL(cvt_f16_kernel, dim3(blocks), dim3(256), 0, stream, (const u32x4*)src[i],
-                         (f16x8*)dst[i], n8);
+      hipLaunchKernelGGL(cvt_f16_kernel, dim3(blocks), dim3(256), 0, stream, (const u32x4*)k,
+                         (f16x8*)k16, n8);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const int nqb16 = (T + 127) / 128;
     hipLaunchKernelGGL((bwd_dq16b_kernel<D>), dim3(nqb16 * B * Hq), dim3(512), 0, stream,
-                       q16, k16, v16, r16, g16, lse, c_aux, G, dl, dq, drho, B, Hq, Hkv, T, scale,
-                       scale * kLog2e);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+                       (const uint16_t*)q, (const uint16_t*)k16, (const uint16_t*)v,
+                       (const uint16_t*)rho, (const uint16_t*)d_o, o, vbar, lse, c_aux, G, dl, q16,
+                       r16, g16, dq, drho, B, Hq, Hkv, T, scale, scale * kLog2e);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv16b_kernel<D>), dim3(nkb * B * Hkv), dim3(512), 0, stream,
-                       q16, k16, v16, r16, g16, lse, c_aux, G, dl, dk, dv, B, Hq, Hkv, T, scale,
-                       scale * kLog2e);
+                       (const uint16_t*)q16, (const uint16_t*)k, (const uint16_t*)v,
+                       (const uint16_t*)r16, (const uint16_t*)g16, lse, c_aux, G, dl, dk, dv, B, Hq,
+                       Hkv, T, scale, scale * kLog2e);
     return hipGetLastError();
   } else {
+    hipLaunchKernelGGL((bwd_pre_kernel<Pol, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
+                       stream, (const in_t*)d_o, o, vbar, G, dl, rows);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_kernel<Pol, D>), dim3(nqb * B * Hq), dim3(BWD_THREADS), 0, stream,
                        (const in_t*)q, (const in_t*)k, (const in_t*)v, (const in_t*)rho,
                        (const in_t*)d_o, lse, c_aux, G, dl, dq, drho, B, Hq, Hkv, T, scale,
@@ -920,11 +953,11 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
 }  // namespace
 
 // Workspace of the backward: G and delta (fp32 per query row), then, for bf16
-// inputs, fp16 copies of q, rho, dO ([B, Hq, T, d]) and K, V ([B, Hkv, T, d]).
+// inputs, fp16 copies of q, rho, dO ([B, Hq, T, d]) and K ([B, Hkv, T, d]).
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int d) {
   const size_t rows = (size_t)B * Hq * T;
   return bwd_ws_align(2 * rows * sizeof(float)) +
-         (3 * rows * d + 2 * (size_t)B * Hkv * T * d) * sizeof(uint16_t);
+         (3 * rows * d + (size_t)B * Hkv * T * d) * sizeof(uint16_t);
 }
 
 hipError_t launch_bwd(int dtype, const void* q, const void* k, const void* v, const void* rho,

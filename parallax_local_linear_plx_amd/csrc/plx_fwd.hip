@@ -520,7 +520,14 @@ struct Fwd16Smem {
 };
 
 
-template <int D, int NW>
+// AUX: the launch writes c_aux.  The probe mean c_i = kbar_i . rho_i handed to
+// the backward is then taken from unrounded sums, sum_j p_j r_j / sum_j p_j,
+// carried beside the rounded ones: the rounded C matches the fp16 operands the
+// value MFMAs used (so o stays consistent with U), but its fp16 rounding of
+// p r (|r| up to tens) shifts c by ~1e-2 on rows with few keys, and the
+// backward's dV = sum_i w_ij (1 + c_i - r_ij) dO_i carries that shift
+// straight through.
+template <int D, int NW, bool AUX>
 __global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ rho, float* __restrict__ o, float* __restrict__ lse,
@@ -633,8 +640,9 @@ __global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.f;
   asm volatile("" : "+v"(ones));  // kept in registers, not rebuilt per sub-tile
-  // e_part: this lane's unrounded sum of p (the LSE only)
-  float m_run = -INFINITY, e_part = 0.f;
+  // e_part: this lane's unrounded sum of p (the LSE only); ce_part: the
+  // unrounded sum of p r (c_aux only)
+  float m_run = -INFINITY, e_part = 0.f, ce_part = 0.f;
 
   auto subtile = [&](int kbuf, int vbuf, int st, int kbase) {
     // scores
@@ -701,6 +709,7 @@ __global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
       const float m_u = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = fast_exp2(m_run - m_u);
       e_part *= alpha;
+      if constexpr (AUX) ce_part *= alpha;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         lacc[jj] *= alpha;
@@ -723,8 +732,10 @@ __global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
       const float p0 = fast_exp2(__builtin_fmaf(s0, scale_log2, -m_use));
       const float p1 = fast_exp2(__builtin_fmaf(s1, scale_log2, -m_use));
       e_part += p0 + p1;
+      const float pr0 = p0 * racc[e >> 2][e & 3], pr1 = p1 * racc[e >> 2][(e & 3) + 1];
+      if constexpr (AUX) ce_part += pr0 + pr1;
       const f16x2 ph = {(_Float16)p0, (_Float16)p1};
-      const f16x2 rh = {(_Float16)(p0 * racc[e >> 2][e & 3]), (_Float16)(p1 * racc[e >> 2][(e & 3) + 1])};
+      const f16x2 rh = {(_Float16)pr0, (_Float16)pr1};
       pop[e] = ph[0];
       pop[e + 1] = ph[1];
       prop[e] = rh[0];
@@ -774,6 +785,11 @@ __global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
   float e_tot = e_part;
   e_tot += __shfl_xor(e_tot, 16, 64);
   e_tot += __shfl_xor(e_tot, 32, 64);
+  float ce_tot = ce_part;
+  if constexpr (AUX) {
+    ce_tot += __shfl_xor(ce_tot, 16, 64);
+    ce_tot += __shfl_xor(ce_tot, 32, 64);
+  }
   const float inv = 1.f / l_tot;
   const float cc = c_tot * inv;
   const bool no_icpt = flags & PLX_NO_INTERCEPT;
@@ -807,7 +823,7 @@ __global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
     }
     if (g == 0) {
       if (lse) lse[(size_t)bh * T + my_q] = (m_run + __log2f(e_tot)) * kLn2;
-      if (c_aux) c_aux[(size_t)bh * T + my_q] = cc;
+      if constexpr (AUX) c_aux[(size_t)bh * T + my_q] = ce_tot / e_tot;
       if (cor) cor[(size_t)bh * T + my_q] = __builtin_sqrtf(n_c) / __builtin_sqrtf(n_o);
     }
   }
@@ -818,9 +834,14 @@ hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void*
                         float* lse, float* c_aux, float* vbar_aux, float* cor, unsigned flags, int B,
                         int Hq, int Hkv, int T, float scale, hipStream_t stream) {
   const int nqb = (T + 16 * NW - 1) / (16 * NW);
-  hipLaunchKernelGGL((fwd16_kernel<D, NW>), dim3(nqb * B * Hq), dim3(64 * NW), 0, stream,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)rho, o,
-                     lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale * kLog2e);
+  if (c_aux)
+    hipLaunchKernelGGL((fwd16_kernel<D, NW, true>), dim3(nqb * B * Hq), dim3(64 * NW), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)rho,
+                       o, lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale * kLog2e);
+  else
+    hipLaunchKernelGGL((fwd16_kernel<D, NW, false>), dim3(nqb * B * Hq), dim3(64 * NW), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)rho,
+                       o, lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale * kLog2e);
   return hipGetLastError();
 }
 

@@ -172,10 +172,10 @@ def test_bwd_workspace_size():
     # q, rho, dO ([B, Hq, T, d]) and k, v ([B, Hkv, T, d])
     B, Hq, Hkv, T, d = 8, 16, 8, 4096, 128
     head = (2 * B * Hq * T * 4 + 255) // 256 * 256
-    assert binding.bwd_workspace_size(B, Hq, Hkv, T, d) == head + (3 * B * Hq * T * d + 2 * B * Hkv * T * d) * 2
+    assert binding.bwd_workspace_size(B, Hq, Hkv, T, d) == head + (3 * B * Hq * T * d + B * Hkv * T * d) * 2
     B, Hq, Hkv, T, d = 1, 2, 1, 3, 64
     head = (2 * B * Hq * T * 4 + 255) // 256 * 256
-    assert binding.bwd_workspace_size(B, Hq, Hkv, T, d) == head + (3 * B * Hq * T * d + 2 * B * Hkv * T * d) * 2
+    assert binding.bwd_workspace_size(B, Hq, Hkv, T, d) == head + (3 * B * Hq * T * d + B * Hkv * T * d) * 2
     assert binding.bwd_workspace_size(8, 16, 8, 0, 128) == 0
 
 

@@ -47,6 +47,7 @@ def test_fp32_gqa_ragged(gpu_lib, B, Hq, Hkv, T, d):
     check_fp32(got["o"], ref["o"], "o")
     check_fp32(got["lse"], ref["lse"], "lse")
     check_fp32(got["vbar"], ref["o_sa"], "vbar")
+    check_fp32(got["c"], ref["c"], "c")
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,T,d,proj", [
@@ -58,10 +59,16 @@ def test_fp32_gqa_ragged(gpu_lib, B, Hq, Hkv, T, d):
 def test_bf16_against_oracle(gpu_lib, B, Hq, Hkv, T, d, proj):
     say(f"case bf16 B{B} Hq{Hq} Hkv{Hkv} T{T} d{d} projected-rho={proj}")
     wl = inputs.make_prefill(B, Hq, Hkv, T, d, dtype="bf16", seed=41 + T, rho_projected=proj)
-    got = _run(wl)
+    got = _run(wl, aux=True)
     ref = _oracle(wl)
     check_bf16(got["o"], ref["o"], "o")
+    check_bf16(got["vbar"], ref["o_sa"], "vbar")
     assert np.max(np.abs(got["lse"] - ref["lse"])) <= LSE_ABS
+    # the auxiliary c = kbar . rho the backward consumes: from unrounded sums,
+    # so it is accurate to fp32 rounding of sum p r / sum p, |r| up to ~50
+    err_c = np.abs(got["c"] - ref["c"])
+    say(f"  c: max-abs {err_c.max():.3e}  max|ref| {np.abs(ref['c']).max():.3e}")
+    assert np.all(err_c <= 1e-4 * np.maximum(np.abs(ref["c"]), 1.0)), float(err_c.max())
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

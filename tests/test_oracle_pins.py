@@ -333,3 +333,21 @@ def test_kv_row_gradients_match_full_backward():
     for n, (b, hk, j) in enumerate(keys):
         np.testing.assert_allclose(dk[n], full["dk"][b, hk, j], rtol=0, atol=1e-13)
         np.testing.assert_allclose(dv[n], full["dv"][b, hk, j], rtol=0, atol=1e-13)
+
+
+def test_probe_mean_c_is_softmax_weighted_probe_score():
+    """c_i = kbar_i . rho_i equals sum_j w_ij (rho_i . k_j), with w from torch's
+    causal softmax (fp64)."""
+    g = _rng(23)
+    B, Hq, Hkv, T, d = 1, 4, 2, 21, 6
+    q = g.standard_normal((B, Hq, T, d))
+    k = g.standard_normal((B, Hkv, T, d))
+    v = g.standard_normal((B, Hkv, T, d))
+    rho = g.standard_normal((B, Hq, T, d))
+    out = orc.prefill_forward(q, k, v, rho, 0.4)
+    kk = torch.from_numpy(np.repeat(k, 2, axis=1))
+    s = 0.4 * torch.from_numpy(q) @ kk.transpose(-1, -2)
+    s = s.masked_fill(~torch.ones(T, T, dtype=torch.bool).tril(), float("-inf"))
+    w = torch.softmax(s, dim=-1)
+    r = torch.from_numpy(rho) @ kk.transpose(-1, -2)
+    np.testing.assert_allclose(out["c"], (w * r).sum(-1).numpy(), rtol=0, atol=1e-12)
