@@ -156,6 +156,31 @@ plx_status plx_decode(const void* q, const void* rho, const void* k_cache, const
                       void* workspace, size_t workspace_bytes, plx_dtype dtype, plx_stream stream);
 
 /*
+ * Decode with no workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  It computes exactly what plx_decode computes (same
+ * kernels, same schedule, bitwise the same results) and takes the same
+ * arguments less the workspace.  The partial records go to a buffer inside the
+ * library instead: one static device array of PLX_DECODE_SCRATCH_BYTES per GPU,
+ * whose address is resolved on the first call made with that GPU current and
+ * which that GPU holds until the process ends.  The call allocates and frees
+ * nothing.
+ *   Size limit: plx_decode_workspace_size(B, Hq, Hkv, S_max, d, num_splits) must
+ *   not exceed PLX_DECODE_SCRATCH_BYTES; larger problems return
+ *   PLX_ERR_WORKSPACE before anything is launched (use plx_decode with a
+ *   caller-owned workspace for them).
+ *   Sharing: every call on one GPU uses that GPU's single array, which keeps
+ *   the last call's records.  Calls whose executions overlap on the same GPU
+ *   (different streams, threads or processes' graphs replayed concurrently)
+ *   race on it and give wrong results; serialise them, e.g. on one stream.
+ */
+#define PLX_DECODE_SCRATCH_BYTES (16u << 20)
+plx_status plx_decode_noalloc(const void* q, const void* rho, const void* k_cache,
+                              const void* v_cache, const int32_t* ctx_len, float* o, float* lse,
+                              int B, int Hq, int Hkv, int S_max, int d, float scale, int num_splits,
+                              plx_dtype dtype, plx_stream stream);
+
+/*
  * Family corners and the correction-to-output ratio.
  *
  * The pages place Parallax in a family of attention operators spanned by three

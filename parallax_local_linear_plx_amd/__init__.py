@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     plx_bwd,
     plx_decode,
     plx_decode_ex,
+    plx_decode_noalloc,
     plx_fwd_prefill,
     plx_fwd_prefill_ex,
     plx_qkvr_proj,

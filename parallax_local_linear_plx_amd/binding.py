@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
     L.plx_decode.restype = _i
     L.plx_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _i, _i, _i, _i, _i, _f, _i, _vp, _sz, _i, _vp]
+    L.plx_decode_noalloc.restype = _i
+    L.plx_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _i, _i, _i, _i, _i, _f, _i, _i, _vp]
     L.plx_qkvr_proj.restype = _i
     L.plx_qkvr_proj.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]
     L.plx_bwd_workspace_size.restype = _sz
@@ -256,6 +259,46 @@ def _decode(q, rho, k_cache, v_cache, ctx_len, scale, *, num_splits, workspace, 
         _check(st, "plx_decode_ex")
         if cor_t is not None:
             out["cor"] = cor_t
+    if lse_t is not None:
+        out["lse"] = lse_t
+    return out
+
+
+# Size limit of plx_decode_noalloc's records (PLX_DECODE_SCRATCH_BYTES).
+DECODE_SCRATCH_BYTES = 16 << 20
+
+
+def plx_decode_noalloc(q, rho, k_cache, v_cache, ctx_len, scale=None, *, num_splits=0, o=None,
+                       lse=True):
+    """Decode with the partial records in the library's own per-GPU buffer
+    (no workspace argument; the C call allocates nothing).  Same arguments and
+    results as ``plx_decode``; calls that overlap on one GPU race.  Outputs not
+    supplied are allocated here, by torch, before the call."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError(f"q must be [B, Hq, d] and the caches [B, Hkv, S_max, d]; got "
+                         f"{tuple(q.shape)} and {tuple(k_cache.shape)}")
+    B, Hq, d = q.shape
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    _need(q, "q", (B, Hq, d), q.dtype, dev)
+    _need(rho, "rho", (B, Hq, d), q.dtype, dev)
+    _need(k_cache, "k_cache", (B, Hkv, S_max, d), q.dtype, dev)
+    _need(v_cache, "v_cache", (B, Hkv, S_max, d), q.dtype, dev)
+    _need(ctx_len, "ctx_len", (B,), torch.int32, dev)
+    if o is not None:
+        _need(o, "o", (B, Hq, d), torch.float32, dev)
+    _need_gpu(dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    lse_t = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse else None
+    st = lib().plx_decode_noalloc(_ptr(q), _ptr(rho), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_len),
+                                  _ptr(o), _ptr(lse_t), B, Hq, Hkv, S_max, d, float(scale),
+                                  int(num_splits), _dtype_code(q), _stream(dev))
+    _check(st, "plx_decode_noalloc")
+    out = {"o": o}
     if lse_t is not None:
         out["lse"] = lse_t
     return out

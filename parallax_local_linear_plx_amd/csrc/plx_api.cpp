@@ -91,11 +91,11 @@ size_t plx_decode_workspace_size(int B, int Hq, int Hkv, int S_max, int d, int n
   return bytes;
 }
 
-plx_status plx_decode_ex(const void* q, const void* rho, const void* k_cache, const void* v_cache,
-                         const int32_t* ctx_len, float* o, float* lse, float* cor, int B, int Hq,
-                         int Hkv, int S_max, int d, float scale, int num_splits, unsigned flags,
-                         void* workspace, size_t workspace_bytes, plx_dtype dtype,
-                         plx_stream stream) {
+// Arguments of the decode entry points other than the workspace.
+static plx_status check_decode(const void* q, const void* rho, const void* k_cache, const void* v_cache,
+                        const int32_t* ctx_len, const float* o, const float* lse, const float* cor,
+                        int B, int Hq, int Hkv, int S_max, int d, float scale, int num_splits,
+                        unsigned flags, plx_dtype dtype) {
   if (!q || !rho || !k_cache || !v_cache || !ctx_len || !o) return PLX_ERR_INVALID_ARG;
   if (!dtype_ok(dtype) || S_max < 1 || num_splits < 0 || !scale_ok(scale) || !flags_ok(flags))
     return PLX_ERR_INVALID_ARG;
@@ -105,9 +105,20 @@ plx_status plx_decode_ex(const void* q, const void* rho, const void* k_cache, co
   if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return PLX_ERR_UNSUPPORTED;
   if (!size_ok((long long)B * Hkv * S_max, d)) return PLX_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(rho) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      !aligned16(o) || (workspace && !aligned16(workspace)) || !aligned4(ctx_len) || !aligned4(lse) ||
-      !aligned4(cor))
+      !aligned16(o) || !aligned4(ctx_len) || !aligned4(lse) || !aligned4(cor))
     return PLX_ERR_INVALID_ARG;
+  return PLX_OK;
+}
+
+plx_status plx_decode_ex(const void* q, const void* rho, const void* k_cache, const void* v_cache,
+                         const int32_t* ctx_len, float* o, float* lse, float* cor, int B, int Hq,
+                         int Hkv, int S_max, int d, float scale, int num_splits, unsigned flags,
+                         void* workspace, size_t workspace_bytes, plx_dtype dtype,
+                         plx_stream stream) {
+  plx_status st = check_decode(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, B, Hq, Hkv, S_max, d,
+                               scale, num_splits, flags, dtype);
+  if (st != PLX_OK) return st;
+  if (workspace && !aligned16(workspace)) return PLX_ERR_INVALID_ARG;
   const size_t need = plx_decode_workspace_size(B, Hq, Hkv, S_max, d, num_splits);
   if (!workspace || workspace_bytes < need) return PLX_ERR_WORKSPACE;
   return from_hip(plx::launch_decode(dtype, q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B,
@@ -121,6 +132,19 @@ plx_status plx_decode(const void* q, const void* rho, const void* k_cache, const
                       size_t workspace_bytes, plx_dtype dtype, plx_stream stream) {
   return plx_decode_ex(q, rho, k_cache, v_cache, ctx_len, o, lse, nullptr, B, Hq, Hkv, S_max, d,
                        scale, num_splits, 0u, workspace, workspace_bytes, dtype, stream);
+}
+
+plx_status plx_decode_noalloc(const void* q, const void* rho, const void* k_cache,
+                              const void* v_cache, const int32_t* ctx_len, float* o, float* lse,
+                              int B, int Hq, int Hkv, int S_max, int d, float scale, int num_splits,
+                              plx_dtype dtype, plx_stream stream) {
+  plx_status st = check_decode(q, rho, k_cache, v_cache, ctx_len, o, lse, nullptr, B, Hq, Hkv, S_max,
+                               d, scale, num_splits, 0u, dtype);
+  if (st != PLX_OK) return st;
+  if (plx_decode_workspace_size(B, Hq, Hkv, S_max, d, num_splits) > PLX_DECODE_SCRATCH_BYTES)
+    return PLX_ERR_WORKSPACE;
+  return from_hip(plx::launch_decode_noalloc(dtype, q, rho, k_cache, v_cache, ctx_len, o, lse, B, Hq,
+                                             Hkv, S_max, d, scale, num_splits, (hipStream_t)stream));
 }
 
 size_t plx_bwd_workspace_size(int B, int Hq, int Hkv, int T, int d) {

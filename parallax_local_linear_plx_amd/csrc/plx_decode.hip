@@ -20,6 +20,9 @@
 // Kernel 2 (merge): per (b, h) rescales the records to a common max and
 // finishes  o = (O/l)(1 + C/l) - U/l,  LSE = M + ln e  (and, on request, the
 // no-intercept output -U/l and the correction-to-output ratio).
+#include <atomic>
+#include <mutex>
+
 #include "plx_common.hpp"
 #include "plx_kernels.hpp"
 
@@ -992,6 +995,55 @@ hipError_t launch_decode(int dtype, const void* q, const void* rho, const void* 
   if (d == 64)
     return launch_decode_t<PolF32, 64>(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, scale, chunk, nsplit, partials, stream);
   return launch_decode_t<PolF32, 128>(q, rho, k_cache, v_cache, ctx_len, o, lse, cor, flags, B, Hq, Hkv, S_max, scale, chunk, nsplit, partials, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Records for plx_decode_noalloc: a static device array, one per GPU (each GPU
+// the library runs on holds its own copy until the process ends).  In host
+// code `decode_scratch` names a host-side stand-in, not the device array, so
+// its device address is asked for once per device (hipGetSymbolAddress, with
+// that device current) and only that address is handed to the kernels.
+static __device__ __align__(256) float decode_scratch[PLX_DECODE_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+hipError_t scratch_for_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      e = hipGetSymbolAddress(&addr, HIP_SYMBOL(decode_scratch));
+      if (e != hipSuccess) return e;
+      if (!addr) return hipErrorInvalidSymbol;
+      p = static_cast<float*>(addr);
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_decode_noalloc(int dtype, const void* q, const void* rho, const void* k_cache,
+                                 const void* v_cache, const int32_t* ctx_len, float* o, float* lse,
+                                 int B, int Hq, int Hkv, int S_max, int d, float scale,
+                                 int num_splits, hipStream_t stream) {
+  float* part = nullptr;
+  const hipError_t e = scratch_for_current_device(&part);
+  if (e != hipSuccess) return e;
+  // the records need no clearing: the merge reads only records this call's
+  // partial kernel writes (contents on entry are ignored, as for plx_decode)
+  return launch_decode(dtype, q, rho, k_cache, v_cache, ctx_len, o, lse, nullptr, 0u, B, Hq, Hkv,
+                       S_max, d, scale, num_splits, part, stream);
 }
 
 }  // namespace plx

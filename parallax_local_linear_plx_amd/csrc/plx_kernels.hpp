@@ -27,6 +27,13 @@ hipError_t launch_decode(int dtype, const void* q, const void* rho, const void* 
                          float* cor, unsigned flags, int B, int Hq, int Hkv, int S_max, int d,
                          float scale, int num_splits, float* partials, hipStream_t stream);
 
+// Decode with the records in the library's own per-device scratch array
+// (PLX_DECODE_SCRATCH_BYTES); the caller has checked the size.
+hipError_t launch_decode_noalloc(int dtype, const void* q, const void* rho, const void* k_cache,
+                                 const void* v_cache, const int32_t* ctx_len, float* o, float* lse,
+                                 int B, int Hq, int Hkv, int S_max, int d, float scale,
+                                 int num_splits, hipStream_t stream);
+
 // Backward: workspace bytes (G and delta, then the fp16 input copies of the bf16 path).
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int d);
 hipError_t launch_bwd(int dtype, const void* q, const void* k, const void* v, const void* rho,

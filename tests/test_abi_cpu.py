@@ -308,3 +308,22 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError, match="GPU tensors only"):
         plx_fwd_prefill(q, k, k, q)
     assert torch.zeros(1).device.type == "cpu"
+
+
+def test_decode_noalloc_refuses_problems_beyond_its_buffer():
+    """plx_decode_noalloc keeps its records in a fixed per-GPU array of
+    PLX_DECODE_SCRATCH_BYTES; a problem needing more is refused before any HIP
+    call, with the workspace status.  Other validation matches plx_decode."""
+    L = binding.lib()
+    i32 = ctypes.c_int
+    args = lambda B, Hq, Hkv, S, d, ns, dtype=binding.PLX_BF16: (  # noqa: E731
+        FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, B, Hq, Hkv, S, d, ctypes.c_float(0.1), ns, dtype, None)
+    big = (64, 16, 1, 1 << 16, 128, 256)
+    assert binding.decode_workspace_size(*big) > binding.DECODE_SCRATCH_BYTES
+    assert L.plx_decode_noalloc(*args(*big)) == binding.PLX_ERR_WORKSPACE
+    assert L.plx_decode_noalloc(*args(2, 6, 2, 64, 128, 0)) == binding.PLX_ERR_UNSUPPORTED  # G = 3
+    assert L.plx_decode_noalloc(*args(2, 4, 2, 0, 128, 0)) == binding.PLX_ERR_INVALID_ARG
+    a = list(args(2, 4, 2, 64, 128, 0))
+    a[0] = None
+    assert L.plx_decode_noalloc(*a) == binding.PLX_ERR_INVALID_ARG
+    assert i32(binding.DECODE_SCRATCH_BYTES).value == 16 << 20
