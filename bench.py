@@ -137,12 +137,12 @@ def bench_prefill(steps, warmup):
 
 
 # ------------------------------------------------------------------- decode
-def bench_decode(steps, warmup, B, ctx_len, S_max, name, seed, graph=True):
+def bench_decode(steps, warmup, B, ctx_len, S_max, name, seed, graph=True, Hq=16, Hkv=8):
     import torch
 
     from parallax_local_linear_plx_amd import inputs, plx_decode
 
-    Hq, Hkv, d = 16, 8, 128
+    d = 128
     kc = inputs.device_normal((B, Hkv, S_max, d), 1.0, seed)
     vc = inputs.device_normal((B, Hkv, S_max, d), 1.0, seed + 1)
     q = inputs.device_normal((B, Hq, d), 1.0, seed + 2)
@@ -421,6 +421,7 @@ KERNEL_SOURCES = {
     "prefill": ["plx_fwd.hip", "plx_common.hpp"],
     "decode": ["plx_decode.hip", "plx_common.hpp"],
     "decode_long": ["plx_decode.hip", "plx_common.hpp"],
+    "decode_g16": ["plx_decode.hip", "plx_common.hpp"],
     "bwd": ["plx_bwd.hip", "plx_common.hpp"],
     "proj": ["plx_proj.hip", "plx_common.hpp"],
 }
@@ -528,8 +529,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--only", default="all",
-                    choices=["all", "prefill", "decode", "decode_long", "train", "proj", "copy",
-                             "decode_sweep", "headdim", "peaks"])
+                    choices=["all", "prefill", "decode", "decode_long", "decode_g16", "train", "proj",
+                             "copy", "decode_sweep", "headdim", "peaks"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay decode timing")
     args = ap.parse_args()
@@ -587,6 +588,14 @@ def main():
                                           "bf16 long-context decode B=8 Hq=16 Hkv=8 "
                                           "ctx~U{16384..131072} d=128, split-K", 41, not args.no_graph)
         log(f"  {res['decode_long']['us_per_step']:.1f} us  {res['decode_long']['GB/s']:.0f} GB/s")
+    if args.only in ("all", "decode_g16"):
+        # sixteen query heads per KV head: the kernel's two column groups share
+        # one pass over the cache
+        log("decode B64 Hq16 Hkv1 ctx8192 ...")
+        res["decode_g16"] = bench_decode(args.steps, args.warmup, 64, [8192] * 64, 8192,
+                                         "bf16 decode B=64 Hq=16 Hkv=1 (G=16) ctx=8192 d=128", 35,
+                                         not args.no_graph, Hq=16, Hkv=1)
+        log(f"  {res['decode_g16']['us_per_step']:.1f} us  {res['decode_g16']['GB/s']:.0f} GB/s")
     if args.only in ("all", "proj"):
         log("stacked projection ...")
         res["proj"] = bench_proj(args.steps, args.warmup)
@@ -621,7 +630,7 @@ def main():
                                   "algorithmic_flops_per_launch": p["flops"]}})
     else:
         line.update({"value": None, "unit": "TFLOP/s", "ms_per_step": None, "config": {"workload": args.only}})
-    for key in ("decode", "decode_long", "train", "proj"):
+    for key in ("decode", "decode_long", "decode_g16", "train", "proj"):
         if key in res:
             line[key] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res[key].items()}
             if key.startswith("decode"):
@@ -630,7 +639,8 @@ def main():
                     "bound": "hbm", "achieved": round(r["GB/s"], 1), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(r["GB/s"] / PEAK_HBM_GBS, 4),
                     "traffic": measured_traffic(key),
-                    "kernel": "decode16_balanced_kernel<128,2> + decode_merge_balanced_kernel<128>",
+                    "kernel": (f"decode16_balanced_kernel<128,{16 if key == 'decode_g16' else 2}> + "
+                               "decode_merge_balanced_kernel<128>"),
                     **({"measured_peak": peaks["hbm_read_gbs"],
                         "frac_of_measured": round(r["GB/s"] / peaks["hbm_read_gbs"], 4)} if peaks else {}),
                     "algorithmic_bytes_per_launch": r["bytes"]}

@@ -38,8 +38,7 @@
  *     score must satisfy |r_ij| = |rho_i . k_j| <= 4094 (fp16's largest
  *     value over 16).  The workloads' probes give |r| of a few tens.
  *   - Supported head dims: d = 64 or 128 (d_k = d_v = d) everywhere; d = 256 as
- *     well for bf16 in plx_fwd_prefill(_ex), plx_decode(_ex) and plx_qkvr_proj
- *     (PLX_ERR_UNSUPPORTED for fp32 and for plx_bwd).
+ *     well for every bf16 call (PLX_ERR_UNSUPPORTED for fp32 at d = 256).
  *   - All pointers are DEVICE pointers unless stated.  The caller owns every
  *     buffer; the library never allocates or frees device memory and keeps no
  *     state between calls.  Calls are asynchronous on `stream` (a hipStream_t;

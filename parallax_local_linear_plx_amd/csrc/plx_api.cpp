@@ -16,7 +16,8 @@ bool flags_ok(unsigned f) { return (f & ~(PLX_UNIFORM_WEIGHTS | PLX_NO_INTERCEPT
 
 bool dtype_ok(plx_dtype dt) { return dt == PLX_F32 || dt == PLX_BF16; }
 
-// d = 256 is served by the bf16 forward, decode and projection kernels only.
+// d = 256 is served by the bf16 kernels (forward, decode, backward, projection);
+// the fp32 kernels stop at d = 128.
 plx_status check_heads(int B, int Hq, int Hkv, int d, plx_dtype dtype, bool allow256) {
   if (B < 1 || Hq < 1 || Hkv < 1) return PLX_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return PLX_ERR_INVALID_ARG;
@@ -149,7 +150,7 @@ plx_status plx_decode_noalloc(const void* q, const void* rho, const void* k_cach
 
 size_t plx_bwd_workspace_size(int B, int Hq, int Hkv, int T, int d) {
   if (B < 1 || Hq < 1 || Hkv < 1 || T < 1) return 0;
-  if (d != 64 && d != 128) return 0;
+  if (!dim_ok(d)) return 0;
   // G_i = dO_i . o_i and delta_i = dO_i . vbar_i (fp32 each), then the fp16
   // copies of q, rho, dO, k and v that the bf16 path's kernels read
   return plx::bwd_workspace_bytes(B, Hq, Hkv, T, d);
@@ -163,7 +164,7 @@ plx_status plx_bwd(const void* q, const void* k, const void* v, const void* rho,
   if (!q || !k || !v || !rho || !d_o || !o || !lse || !c_aux || !vbar_aux) return PLX_ERR_INVALID_ARG;
   if (!dq || !dk || !dv || !drho) return PLX_ERR_INVALID_ARG;
   if (!dtype_ok(dtype) || T < 1 || !scale_ok(scale)) return PLX_ERR_INVALID_ARG;
-  plx_status st = check_heads(B, Hq, Hkv, d, dtype, false);
+  plx_status st = check_heads(B, Hq, Hkv, d, dtype, true);
   if (st != PLX_OK) return st;
   if (!size_ok((long long)B * Hq * T, d)) return PLX_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, rho, d_o, o, vbar_aux, dq, dk, dv, drho};

@@ -440,26 +440,29 @@ __global__ __launch_bounds__(256) void cvt_f16_kernel(const u32x4* __restrict__ 
 // for the rows it owns: G_i = dO_i . o_i, delta_i = dO_i . vbar_i, and fp16
 // copies of q_i, rho_i and dO_i (the key-outer kernel's LDS tiles), so no
 // separate pass reads dO, o and vbar.
-constexpr int DQB_BC = 128;
-template <int D>
+// Shape per head dim (bwd16_shape): d <= 128 runs 8 waves (two per SIMD) on
+// 128-key tiles; d = 256 runs 4 waves (one per SIMD: its doubled operands and
+// accumulators need the whole register file) on 32-key tiles, which keeps the
+// double-buffered tiles and their staging registers within LDS and registers.
+template <int D, int BC>
 struct DqbSmem {
   static constexpr int LD = D + 16;  // as the forward's tiles: conflict-free rows and transpose reads
-  alignas(16) _Float16 k[2][DQB_BC * LD];
-  alignas(16) uint16_t v[2][DQB_BC * LD];  // bf16, as stored
+  alignas(16) _Float16 k[2][BC * LD];
+  alignas(16) uint16_t v[2][BC * LD];  // bf16, as stored
 };
 
-template <int D>
-__global__ __launch_bounds__(512, 1) void bwd_dq16b_kernel(
+template <int D, int NW, int BC>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k16, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ rho, const uint16_t* __restrict__ d_o, const float* __restrict__ o,
     const float* __restrict__ vbar, const float* __restrict__ lse, const float* __restrict__ c_aux,
     float* __restrict__ Gv, float* __restrict__ dlt, _Float16* __restrict__ q16,
     _Float16* __restrict__ r16, _Float16* __restrict__ g16, float* __restrict__ dq,
     float* __restrict__ drho, int B, int Hq, int Hkv, int T, float scale, float scale_log2) {
-  constexpr int NW = 8, NT = 64 * NW, BR = 16 * NW;
+  constexpr int NT = 64 * NW, BR = 16 * NW;
   constexpr int NS = D / 32, ND = D / 16, CPR = D / 8;
-  constexpr int NCH = DQB_BC * CPR / NT;  // 16-byte chunks per thread per tile and tensor
-  using SM = DqbSmem<D>;
+  constexpr int NCH = BC * CPR / NT;  // 16-byte chunks per thread per tile and tensor
+  using SM = DqbSmem<D, BC>;
   __shared__ SM sm;
 
   const int nqb = (T + BR - 1) / BR;
@@ -481,7 +484,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16b_kernel(
   const uint16_t* kp = k16 + ((size_t)(b * Hkv + hk) * T) * D;
   const uint16_t* vp = v + ((size_t)(b * Hkv + hk) * T) * D;
   const int kend = min(T, q0 + BR);
-  const int ntiles = (kend + DQB_BC - 1) / DQB_BC;
+  const int ntiles = (kend + BC - 1) / BC;
   const int nsub = (min(kend, qw + 16) + 31) / 32;
 
   // global -> register staging of one tile (rows past T read row T-1: finite,
@@ -624,12 +627,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16b_kernel(
   };
 
   auto iter = [&](int j, int buf) {
-    const int key0 = j * DQB_BC;
-    if (j + 1 < ntiles) gload(key0 + DQB_BC);
+    const int key0 = j * BC;
+    if (j + 1 < ntiles) gload(key0 + BC);
 #pragma unroll
-    for (int st = 0; st < DQB_BC / 32; ++st) {
+    for (int st = 0; st < BC / 32; ++st) {
       const int kbase = key0 + 32 * st;
-      if (4 * j + st < nsub) {
+      if ((BC / 32) * j + st < nsub) {
         if (kbase + 31 > qw)
           subtile(buf, st, kbase, std::true_type{});
         else
@@ -673,27 +676,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dq16b_kernel(
 //   A = Q^T / rho^T / dO^T from transpose reads of the query tiles.
 // Workgroup: 8 waves, 128 keys of one KV head; the 64-row query tiles of all G
 // query heads form one sequence, double-buffered in LDS, one barrier per tile.
-constexpr int DKB_BQ = 64;
-template <int D>
+template <int D, int BQ>
 struct DkbSmem {
   static constexpr int LD = D + 16;
-  alignas(16) _Float16 q[2][DKB_BQ * LD];
-  alignas(16) _Float16 r[2][DKB_BQ * LD];
-  alignas(16) _Float16 g[2][DKB_BQ * LD];
-  alignas(16) float sc[2][4][DKB_BQ];  // per query row: lse * log2e, 1 + c, G + delta c, delta
+  alignas(16) _Float16 q[2][BQ * LD];
+  alignas(16) _Float16 r[2][BQ * LD];
+  alignas(16) _Float16 g[2][BQ * LD];
+  alignas(16) float sc[2][4][BQ];  // per query row: lse * log2e, 1 + c, G + delta c, delta
 };
 
-template <int D>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv16b_kernel(
+template <int D, int NW, int BQ>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ rho, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
     const float* __restrict__ c_aux, const float* __restrict__ Gv, const float* __restrict__ dlt,
     float* __restrict__ dk, float* __restrict__ dv, int B, int Hq, int Hkv, int T, float scale,
     float scale_log2) {
-  constexpr int NW = 8, NT = 64 * NW, BK = 16 * NW;
+  constexpr int NT = 64 * NW, BK = 16 * NW;
   constexpr int NS = D / 32, ND = D / 16, CPR = D / 8;
-  constexpr int NCH = DKB_BQ * CPR / NT;  // 16-byte chunks per thread per tile and tensor
-  using SM = DkbSmem<D>;
+  constexpr int NCH = BQ * CPR / NT;  // 16-byte chunks per thread per tile and tensor
+  using SM = DkbSmem<D, BQ>;
   __shared__ SM sm;
 
   const int bhk_count = B * Hkv;
@@ -710,14 +712,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16b_kernel(
   const bool kvalid = my_k < T;
 
   const size_t kvbase = (size_t)bhk * T;
-  const int nqt = (T - k0 + DKB_BQ - 1) / DKB_BQ;  // query tiles per head (queries >= k0)
+  const int nqt = (T - k0 + BQ - 1) / BQ;  // query tiles per head (queries >= k0)
   const int ntile = G * nqt;
 
   u32x4 pq[NCH], pr[NCH], pg[NCH];
   float psc[4];
   auto tile_rows = [&](int n, size_t& rowbase, int& qt0) {
     const int hh = n / nqt;
-    qt0 = k0 + (n - hh * nqt) * DKB_BQ;
+    qt0 = k0 + (n - hh * nqt) * BQ;
     rowbase = ((size_t)b * Hq + hk * G + hh) * T;
   };
   auto gload = [&](int n) {
@@ -732,7 +734,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16b_kernel(
       pr[i] = *reinterpret_cast<const u32x4*>(rho + off);
       pg[i] = *reinterpret_cast<const u32x4*>(d_o + off);
     }
-    if (threadIdx.x < DKB_BQ) {
+    if (threadIdx.x < BQ) {
       const size_t r = rowbase + min(qt0 + (int)threadIdx.x, T - 1);
       psc[0] = lse[r];
       psc[1] = c_aux[r];
@@ -749,7 +751,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16b_kernel(
       *reinterpret_cast<u32x4*>(&sm.r[buf][o]) = pr[i];
       *reinterpret_cast<u32x4*>(&sm.g[buf][o]) = pg[i];
     }
-    if (threadIdx.x < DKB_BQ) {
+    if (threadIdx.x < BQ) {
       sm.sc[buf][0][threadIdx.x] = psc[0] * kLog2e;
       sm.sc[buf][1][threadIdx.x] = 1.f + psc[1];
       sm.sc[buf][2][threadIdx.x] = psc[2] + psc[3] * psc[1];
@@ -860,7 +862,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv16b_kernel(
     tile_rows(n, rowbase_unused, qt0);
     if (n + 1 < ntile) gload(n + 1);
 #pragma unroll
-    for (int st = 0; st < DKB_BQ / 32; ++st) {
+    for (int st = 0; st < BQ / 32; ++st) {
       const int qs = qt0 + 32 * st;
       if (qs + 31 < kw) continue;  // every query of the sub-tile precedes every key of the wave
       if (qs < kw + 15 || qs + 31 >= T)
@@ -921,13 +923,16 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
                          (f16x8*)k16, n8);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const int nqb16 = (T + 127) / 128;
-    hipLaunchKernelGGL((bwd_dq16b_kernel<D>), dim3(nqb16 * B * Hq), dim3(512), 0, stream,
+    // waves per workgroup and tile sizes: see DqbSmem
+    constexpr int NW = D > 128 ? 4 : 8, BC = D > 128 ? 32 : 128, BQ = D > 128 ? 32 : 64;
+    const int nqb16 = (T + 16 * NW - 1) / (16 * NW);
+    const int nkb16 = (T + 16 * NW - 1) / (16 * NW);
+    hipLaunchKernelGGL((bwd_dq16b_kernel<D, NW, BC>), dim3(nqb16 * B * Hq), dim3(64 * NW), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k16, (const uint16_t*)v,
                        (const uint16_t*)rho, (const uint16_t*)d_o, o, vbar, lse, c_aux, G, dl, q16,
                        r16, g16, dq, drho, B, Hq, Hkv, T, scale, scale * kLog2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv16b_kernel<D>), dim3(nkb * B * Hkv), dim3(512), 0, stream,
+    hipLaunchKernelGGL((bwd_dkdv16b_kernel<D, NW, BQ>), dim3(nkb16 * B * Hkv), dim3(64 * NW), 0, stream,
                        (const uint16_t*)q16, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)r16, (const uint16_t*)g16, lse, c_aux, G, dl, dk, dv, B, Hq,
                        Hkv, T, scale, scale * kLog2e);
@@ -967,6 +972,8 @@ hipError_t launch_bwd(int dtype, const void* q, const void* k, const void* v, co
   if (dtype == PLX_BF16) {
     if (d == 64)
       return launch_bwd_t<PolBF16, 64>(q, k, v, rho, d_o, o, lse, c_aux, vbar_aux, dq, dk, dv, drho, B, Hq, Hkv, T, scale, ws, stream);
+    if (d == 256)
+      return launch_bwd_t<PolBF16, 256>(q, k, v, rho, d_o, o, lse, c_aux, vbar_aux, dq, dk, dv, drho, B, Hq, Hkv, T, scale, ws, stream);
     return launch_bwd_t<PolBF16, 128>(q, k, v, rho, d_o, o, lse, c_aux, vbar_aux, dq, dk, dv, drho, B, Hq, Hkv, T, scale, ws, stream);
   }
   if (d == 64)

@@ -299,16 +299,17 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 constexpr int DEC_NSET = 1;
 constexpr int DEC_BAL_CTAS = 512;  // balanced schedule: at most two workgroups per compute unit
 
-template <int D>
+// NCG column groups of 16: one for up to 8 query heads per KV head, two for 16.
+template <int D, int NCG>
 struct Dec16Smem {
   static constexpr int LD = D + 16;  // row stride: 8 rows of one transpose read hit 8 bank groups
   static constexpr size_t TILE = (size_t)32 * LD;
   static constexpr int MLD = D + 1;
   union {
     uint16_t tiles[DEC_WAVES][TILE];  // per wave: raw bf16 V rows
-    float merge[DEC_WAVES][16 * MLD]; // per wave: [O | U] x column x d
+    float merge[DEC_WAVES][16 * MLD]; // per wave: [O | U] x column x d (one column group at a time)
   };
-  uint16_t bq[16 * D];  // score B operand: [column][d]
+  uint16_t bq[NCG][16 * D];  // score B operands: [column group][column][d]
   float mw[DEC_WAVES][16];
   float wl[DEC_WAVES][16];  // per wave: l (even columns) / C (odd columns)
   float we[DEC_WAVES][16];  // per wave: e
@@ -362,8 +363,12 @@ __device__ long long bal_total(const int32_t* __restrict__ ctx_len, int B, int H
 // One workgroup's pass over keys [k_begin, k_end) of (b, hk) for the G heads
 // hq0 .. hq0+G-1; writes record hh at rec + hh * rec_stride:
 //   [m (log2 units), l, e, C, O[D], U[D]].
+// G = 16 takes two column groups: both B operands are multiplied by every K
+// operand and both sets of value MFMAs share every V operand, so the sixteen
+// heads of a KV head still read its cache once.
 template <int D, int G>
-__device__ __forceinline__ void dec16_range(Dec16Smem<D>& sm, const uint16_t* __restrict__ q,
+__device__ __forceinline__ void dec16_range(Dec16Smem<D, (G > 8 ? 2 : 1)>& sm,
+                                            const uint16_t* __restrict__ q,
                                             const uint16_t* __restrict__ rho,
                                             const uint16_t* __restrict__ kc,
                                             const uint16_t* __restrict__ vc, int b, int hk, int hq0,
@@ -372,34 +377,43 @@ __device__ __forceinline__ void dec16_range(Dec16Smem<D>& sm, const uint16_t* __
                                             size_t rec_stride) {
   constexpr int NS = D / 32;  // 32-deep score steps
   constexpr int ND = D / 16;  // 16-row d tiles of the value accumulators
-  using SM = Dec16Smem<D>;
+  constexpr int NCG = G > 8 ? 2 : 1;  // column groups of 16 (8 heads each)
+  using SM = Dec16Smem<D, NCG>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
 
-  // B operand of the score MFMAs, staged once in LDS: column cc holds q (even)
-  // or rho (odd) of head hq0 + cc/2 (zero for unused columns, and for the q
-  // columns with uniform weights: every score is then exactly 0, p = 1)
+  // B operands of the score MFMAs, staged once in LDS: column cc of group cg
+  // holds q (even) or rho (odd) of head hq0 + 8 cg + cc/2 (zero for unused
+  // columns, and for the q columns with uniform weights: every score is then
+  // exactly 0, p = 1)
   const bool use_q = !(flags & PLX_UNIFORM_WEIGHTS);
-  for (int i = threadIdx.x; i < 16 * D / 8; i += DEC_THREADS) {
-    const int cc = i / (D / 8), d0 = (i % (D / 8)) * 8;
+  for (int i = threadIdx.x; i < NCG * 16 * D / 8; i += DEC_THREADS) {
+    const int cg = i / (16 * D / 8), cc = (i / (D / 8)) % 16, d0 = (i % (D / 8)) * 8;
+    const int head = 8 * cg + (cc >> 1);
     u32x4 raw = {0u, 0u, 0u, 0u};
-    if (cc < 2 * G && ((cc & 1) || use_q)) {
+    if (head < G && ((cc & 1) || use_q)) {
       const uint16_t* src = (cc & 1) ? rho : q;
-      raw = *reinterpret_cast<const u32x4*>(src + ((size_t)b * Hq + hq0 + (cc >> 1)) * D + d0);
+      raw = *reinterpret_cast<const u32x4*>(src + ((size_t)b * Hq + hq0 + head) * D + d0);
     }
-    *reinterpret_cast<u32x4*>(&sm.bq[cc * D + d0]) = raw;
+    *reinterpret_cast<u32x4*>(&sm.bq[cg][cc * D + d0]) = raw;
   }
   __syncthreads();
   const uint16_t* kbase = kc + ((size_t)(b * Hkv + hk) * S_max) * D;
   const uint16_t* vbase = vc + ((size_t)(b * Hkv + hk) * S_max) * D;
   uint16_t* vt = sm.tiles[wave];
 
-  f32x4 ou[ND];
+  f32x4 ou[NCG][ND];
+  float m_run[NCG], l_part[NCG], e_part[NCG];
+  bool used[NCG];
 #pragma unroll
-  for (int i = 0; i < ND; ++i) ou[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f, e_part = 0.f;
-  const bool used = c < 2 * G;
+  for (int cg = 0; cg < NCG; ++cg) {
+#pragma unroll
+    for (int i = 0; i < ND; ++i) ou[cg][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    m_run[cg] = -INFINITY;
+    l_part[cg] = e_part[cg] = 0.f;
+    used[cg] = 8 * cg + (c >> 1) < G;
+  }
   const bool odd = c & 1;
 
   // raw bf16 K and V of one sub-tile: [key tile t][d step s]
@@ -426,15 +440,19 @@ __device__ __forceinline__ void dec16_range(Dec16Smem<D>& sm, const uint16_t* __
   };
 
   auto process = [&](u32x4 (&kx)[2][NS], u32x4 (&vx)[2][NS], int key0) {
-    f32x4 sacc[2];
+    f32x4 sacc[NCG][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      sacc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) sacc[cg][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, kx[t][s]),
-            *reinterpret_cast<const bf16x8_t*>(&sm.bq[c * D + 32 * s + 8 * g]), sacc[t], 0, 0, 0);
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+          sacc[cg][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, kx[t][s]),
+              *reinterpret_cast<const bf16x8_t*>(&sm.bq[cg][c * D + 32 * s + 8 * g]), sacc[cg][t],
+              0, 0, 0);
     }
     // stage the raw V rows; the loaded registers feed only this write and the
     // score MFMAs
@@ -448,47 +466,50 @@ __device__ __forceinline__ void dec16_range(Dec16Smem<D>& sm, const uint16_t* __
     load_sub(kx, vx, key0 + DEC_NSET * DEC_GROUP_KEYS);
     wave_lds_sync();
 
-    // softmax: even columns hold scores, odd columns r
-    float sv[8];
-    float mt = -INFINITY;
+    // softmax per column group: even columns hold scores, odd columns r
+    f16x8 pop[NCG];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int cg = 0; cg < NCG; ++cg) {
+      float sv[8];
+      float mt = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float se = dpp_even_partner(sacc[t][j]);
-        if (key0 + 16 * t + 4 * g + j >= k_end) se = -INFINITY;
-        sv[4 * t + j] = se;
-        mt = fmaxf(mt, se);
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float se = dpp_even_partner(sacc[cg][t][j]);
+          if (key0 + 16 * t + 4 * g + j >= k_end) se = -INFINITY;
+          sv[4 * t + j] = se;
+          mt = fmaxf(mt, se);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt *= scale_log2;
+      if (__any(mt > m_run[cg] + 4.f)) {
+        // lazy rescale (p <= 16 in between; exact after the final normalisation)
+        const float m_new = fmaxf(m_run[cg], mt);
+        const float alpha = fast_exp2(m_run[cg] - m_new);
+        l_part[cg] *= alpha;
+        e_part[cg] *= alpha;
+#pragma unroll
+        for (int i = 0; i < ND; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ou[cg][i][j] *= alpha;
+        m_run[cg] = m_new;
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    mt *= scale_log2;
-    if (__any(mt > m_run + 4.f)) {
-      // lazy rescale (p <= 16 in between; exact after the final normalisation)
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = fast_exp2(m_run - m_new);
-      l_part *= alpha;
-      e_part *= alpha;
+      const float m_use = (m_run[cg] == -INFINITY) ? 0.f : m_run[cg];
+      float lsum = 0.f, esum = 0.f;
 #pragma unroll
-      for (int i = 0; i < ND; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ou[i][j] *= alpha;
-      m_run = m_new;
+      for (int e = 0; e < 8; ++e) {
+        const float p = used[cg] ? fast_exp2(__builtin_fmaf(sv[e], scale_log2, -m_use)) : 0.f;
+        esum += p;
+        const float val = odd ? p * sacc[cg][e >> 2][e & 3] : p;
+        const _Float16 h = (_Float16)val;
+        lsum += (float)h;
+        pop[cg][e] = h;
+      }
+      l_part[cg] += lsum;
+      e_part[cg] += esum;
     }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    f16x8 pop;
-    float lsum = 0.f, esum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = used ? fast_exp2(__builtin_fmaf(sv[e], scale_log2, -m_use)) : 0.f;
-      esum += p;
-      const float val = odd ? p * sacc[e >> 2][e & 3] : p;
-      const _Float16 h = (_Float16)val;
-      lsum += (float)h;
-      pop[e] = h;
-    }
-    l_part += lsum;
-    e_part += esum;
 
     // value MFMAs: A operand V^T from the transpose reads; element e of
     // group g is key 16*(e/4) + 4*g + e%4, matching pop
@@ -502,7 +523,9 @@ __device__ __forceinline__ void dec16_range(Dec16Smem<D>& sm, const uint16_t* __
         av[e] = bf16_bits_to_f16((uint16_t)v0[e]);
         av[4 + e] = bf16_bits_to_f16((uint16_t)v1[e]);
       }
-      ou[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pop, ou[dt], 0, 0, 0);
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg)
+        ou[cg][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pop[cg], ou[cg][dt], 0, 0, 0);
     }
     wave_lds_sync();
   };
@@ -522,57 +545,61 @@ __device__ __forceinline__ void dec16_range(Dec16Smem<D>& sm, const uint16_t* __
   }
 
   // ---- merge the four waves' states through LDS (each wave its own slot,
-  // summed in wave order: the record does not depend on timing) ----
-  __syncthreads();
-  if (g == 0) sm.mw[wave][c] = m_run;
-  __syncthreads();
-  float M = -INFINITY;
+  // summed in wave order: the record does not depend on timing), one column
+  // group at a time ----
 #pragma unroll
-  for (int w = 0; w < DEC_WAVES; ++w) M = fmaxf(M, sm.mw[w][c]);
-  const float sc = (M == -INFINITY) ? 0.f : fast_exp2(m_run - M);
-  float lt = l_part, et = e_part;
-  lt += __shfl_xor(lt, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
-  et += __shfl_xor(et, 16, 64);
-  et += __shfl_xor(et, 32, 64);
-  if (g == 0) {
-    sm.wl[wave][c] = lt * sc;
-    sm.we[wave][c] = et * sc;
-  }
+  for (int cg = 0; cg < NCG; ++cg) {
+    __syncthreads();
+    if (g == 0) sm.mw[wave][c] = m_run[cg];
+    __syncthreads();
+    float M = -INFINITY;
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = 16 * dt + 4 * g + j;
-      sm.merge[wave][c * SM::MLD + d] = ou[dt][j] * sc;
+    for (int w = 0; w < DEC_WAVES; ++w) M = fmaxf(M, sm.mw[w][c]);
+    const float sc = (M == -INFINITY) ? 0.f : fast_exp2(m_run[cg] - M);
+    float lt = l_part[cg], et = e_part[cg];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    et += __shfl_xor(et, 16, 64);
+    et += __shfl_xor(et, 32, 64);
+    if (g == 0) {
+      sm.wl[wave][c] = lt * sc;
+      sm.we[wave][c] = et * sc;
     }
-  __syncthreads();
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 16 * dt + 4 * g + j;
+        sm.merge[wave][c * SM::MLD + d] = ou[cg][dt][j] * sc;
+      }
+    __syncthreads();
 
-  for (int hh = 0; hh < G; ++hh) {
-    float* r = rec + hh * rec_stride;
-    const int c0 = 2 * hh;
-    if (threadIdx.x == 0) {
-      float M0 = -INFINITY, l0 = 0.f, e0 = 0.f, C0 = 0.f;
-      for (int w = 0; w < DEC_WAVES; ++w) {
-        M0 = fmaxf(M0, sm.mw[w][c0]);
-        l0 += sm.wl[w][c0];
-        e0 += sm.we[w][c0];
-        C0 += sm.wl[w][c0 + 1];
+    for (int hl = 0; hl < 8 && 8 * cg + hl < G; ++hl) {
+      float* r = rec + (8 * cg + hl) * rec_stride;
+      const int c0 = 2 * hl;
+      if (threadIdx.x == 0) {
+        float M0 = -INFINITY, l0 = 0.f, e0 = 0.f, C0 = 0.f;
+        for (int w = 0; w < DEC_WAVES; ++w) {
+          M0 = fmaxf(M0, sm.mw[w][c0]);
+          l0 += sm.wl[w][c0];
+          e0 += sm.we[w][c0];
+          C0 += sm.wl[w][c0 + 1];
+        }
+        r[0] = M0;
+        r[1] = l0;
+        r[2] = e0;
+        r[3] = C0;
       }
-      r[0] = M0;
-      r[1] = l0;
-      r[2] = e0;
-      r[3] = C0;
-    }
-    for (int d = threadIdx.x; d < D; d += DEC_THREADS) {
-      float od = 0.f, ud = 0.f;
+      for (int d = threadIdx.x; d < D; d += DEC_THREADS) {
+        float od = 0.f, ud = 0.f;
 #pragma unroll
-      for (int w = 0; w < DEC_WAVES; ++w) {
-        od += sm.merge[w][c0 * SM::MLD + d];
-        ud += sm.merge[w][(c0 + 1) * SM::MLD + d];
+        for (int w = 0; w < DEC_WAVES; ++w) {
+          od += sm.merge[w][c0 * SM::MLD + d];
+          ud += sm.merge[w][(c0 + 1) * SM::MLD + d];
+        }
+        r[4 + d] = od;
+        r[4 + D + d] = ud;
       }
-      r[4 + d] = od;
-      r[4 + D + d] = ud;
     }
   }
   __syncthreads();  // the next range reuses the LDS tiles that alias the merge buffer
@@ -584,7 +611,7 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_chunk_kernel(
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ ctx_len, float* __restrict__ part,
     int Hq, int Hkv, int S_max, int chunk, int nsplit, int hoff, unsigned flags, float scale_log2) {
   constexpr int REC = 2 * D + 4;
-  __shared__ Dec16Smem<D> sm;
+  __shared__ Dec16Smem<D, (G > 8 ? 2 : 1)> sm;
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int ctx = dec_len(ctx_len, b, S_max);
   const int k_begin = split * chunk;
@@ -718,7 +745,7 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_balanced_kernel(
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ ctx_len, float* __restrict__ part,
     int B, int Hq, int Hkv, int S_max, int hoff, unsigned flags, float scale_log2) {
   constexpr int REC = 2 * D + 4;
-  __shared__ Dec16Smem<D> sm;
+  __shared__ Dec16Smem<D, (G > 8 ? 2 : 1)> sm;
   const int lane = threadIdx.x & 63;
   const int Gfull = Hq / Hkv;
   const int P = gridDim.x;
@@ -888,7 +915,8 @@ hipError_t launch_decode_t(const void* q, const void* rho, const void* kc, const
   const int G = Hq / Hkv;
   hipError_t e;
   if constexpr (sizeof(typename Pol::in_t) == 2) {
-    // bf16: 16-column kernel; 16 heads per KV head take two column groups
+    // bf16: 16-column kernel; 16 heads per KV head take two column groups of
+    // the same launch
 #define PLX_P16(GG, HOFF)                                                                          \
   launch_partial16<D, GG>(q, rho, kc, vc, ctx_len, part, B, Hq, Hkv, S_max, chunk, nsplit, HOFF, \
                           flags, scale, stream)
@@ -897,10 +925,7 @@ hipError_t launch_decode_t(const void* q, const void* rho, const void* kc, const
       case 2: e = PLX_P16(2, 0); break;
       case 4: e = PLX_P16(4, 0); break;
       case 8: e = PLX_P16(8, 0); break;
-      default:
-        e = PLX_P16(8, 0);
-        if (e == hipSuccess) e = PLX_P16(8, 8);
-        break;
+      default: e = PLX_P16(16, 0); break;
     }
 #undef PLX_P16
     if (e != hipSuccess) return e;

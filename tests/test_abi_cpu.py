@@ -137,7 +137,8 @@ def _bwd(**kw):
     (dict(dr=None), binding.PLX_ERR_INVALID_ARG),
     (dict(T=-1), binding.PLX_ERR_INVALID_ARG),
     (dict(d=80), binding.PLX_ERR_UNSUPPORTED),
-    (dict(d=256), binding.PLX_ERR_UNSUPPORTED),  # the backward serves d in {64, 128}
+    (dict(d=256, dtype=binding.PLX_F32), binding.PLX_ERR_UNSUPPORTED),  # fp32 stops at d = 128
+    (dict(d=256, ws_bytes=8), binding.PLX_ERR_WORKSPACE),  # bf16 d = 256 is served
     (dict(ws_bytes=8), binding.PLX_ERR_WORKSPACE),
     (dict(ws=None), binding.PLX_ERR_WORKSPACE),
 ])

@@ -193,3 +193,22 @@ def test_bf16_training_full_size(gpu_lib):
     d_o = wl.tensors["d_o"].f64().reshape(wl.B, Hkv, Hq // Hkv, T, wl.d).sum(axis=(2, 3))
     scale_dv = np.abs(got["dv"]).astype(np.float64).sum(axis=2)
     assert np.all(np.abs(sum_dv - d_o) <= 2e-3 * scale_dv + 1e-2), float(np.max(np.abs(sum_dv - d_o)))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T", [(1, 1, 1, 1), (1, 4, 1, 129), (1, 16, 1, 300), (2, 2, 2, 300)])
+def test_bf16_gradients_head_dim_256(gpu_lib, B, Hq, Hkv, T):
+    """d = 256: four waves (one per SIMD) on 32-row / 32-key tiles; G = 1, 4
+    and 16, several tiles and a ragged tail, and the single-row case; every
+    element of every group against the oracle."""
+    say(f"case bwd bf16 d256 B{B} Hq{Hq} Hkv{Hkv} T{T}")
+    wl = inputs.make_prefill(B, Hq, Hkv, T, 256, dtype="bf16", seed=260 + T + Hq, with_grad=True)
+    got = _run(wl)
+    G = Hq // Hkv
+    for b in range(B):
+        for hk in range(Hkv):
+            ref = _group_oracle(wl, b, hk)
+            hs = slice(hk * G, (hk + 1) * G)
+            for n in ("dk", "dv"):
+                check_bf16(got[n][b, hk], ref[n], f"{n} (b={b}, kv head {hk})")
+            for n in ("dq", "drho"):
+                check_bf16(got[n][b, hs], ref[n], f"{n} (b={b}, kv head {hk})")
