@@ -717,10 +717,20 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
 
   u32x4 pq[NCH], pr[NCH], pg[NCH];
   float psc[4];
+  // Tiles are loaded, and then computed, in increasing order n = hh * nqt + i,
+  // so each side keeps its (head, tile) pair as a cursor that advances by one
+  // tile instead of dividing n by nqt.
+  int ld_hh = 0, ld_i = 0, cp_hh = 0, cp_i = 0;
+  auto advance = [&](int n, int& hh, int& i) {
+    if (hh * nqt + i != n && ++i == nqt) {
+      i = 0;
+      ++hh;
+    }
+  };
   auto tile_rows = [&](int n, size_t& rowbase, int& qt0) {
-    const int hh = n / nqt;
-    qt0 = k0 + (n - hh * nqt) * BQ;
-    rowbase = ((size_t)b * Hq + hk * G + hh) * T;
+    advance(n, ld_hh, ld_i);
+    qt0 = k0 + ld_i * BQ;
+    rowbase = ((size_t)b * Hq + hk * G + ld_hh) * T;
   };
   auto gload = [&](int n) {
     size_t rowbase;
@@ -831,10 +841,11 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
           if (qi < my_k || qi >= T) p = 0.f;
         }
         const float r = racc[t][j], A = aacc[t][j];
-        const float tt = d4[j] - A;
-        pop[4 * t + j] = (_Float16)(p * (k14[j] - r));
-        dsop[4 * t + j] = (_Float16)((scale * p) * __builtin_fmaf(A, k14[j], __builtin_fmaf(r, tt, -k24[j])));
-        drop[4 * t + j] = (_Float16)(p * tt);
+        // with f = 1 + c - r:  dS = p [f A + delta r - (G + delta c)],  dR = p (delta - A)
+        const float f = k14[j] - r;
+        pop[4 * t + j] = (_Float16)(p * f);
+        dsop[4 * t + j] = (_Float16)((scale * p) * __builtin_fmaf(A, f, __builtin_fmaf(r, d4[j], -k24[j])));
+        drop[4 * t + j] = (_Float16)(p * (d4[j] - A));
       }
     }
     // gradient MFMAs: A = Q^T / rho^T / dO^T, 16 d rows x 32 queries each
@@ -857,9 +868,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
   };
 
   auto iter = [&](int n, int buf) {
-    size_t rowbase_unused;
-    int qt0;
-    tile_rows(n, rowbase_unused, qt0);
+    advance(n, cp_hh, cp_i);
+    const int qt0 = k0 + cp_i * BQ;
     if (n + 1 < ntile) gload(n + 1);
 #pragma unroll
     for (int st = 0; st < BQ / 32; ++st) {
