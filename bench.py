@@ -49,21 +49,25 @@ CLOCK_WARM_MS = 60.0
 
 
 def warm_clocks(fn, ms=CLOCK_WARM_MS):
-    """Run fn back to back until at least ``ms`` of device time has passed."""
+    """Run fn back to back, with no host synchronisation in between, for at
+    least ``ms`` of device time (the per-call time is estimated from a short
+    probe first, so short calls are not separated by idle gaps)."""
     import torch
 
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    fn()
     start.record()
-    n = 0
-    while True:
+    for _ in range(4):
         fn()
-        n += 1
-        if n in (1, 2, 4) or n % 8 == 0:
-            stop.record()
-            stop.synchronize()
-            if start.elapsed_time(stop) >= ms:
-                return n
+    stop.record()
+    stop.synchronize()
+    per_call = max(start.elapsed_time(stop) / 4, 1e-3)
+    n = int(math.ceil(1.5 * ms / per_call))  # the probe ran at cold clocks: overshoot
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    return n + 5
 
 
 def time_steps(fn, steps, warmup):
