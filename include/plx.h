@@ -271,9 +271,17 @@ plx_status plx_qkvr_proj(const void* x, const void* w, void* q, void* k, void* v
  *   dq, drho    [B, Hq, T, d]  fp32, written (overwritten, not accumulated)
  *   dk, dv      [B, Hkv, T, d] fp32, written (overwritten, not accumulated)
  *   workspace   at least plx_bwd_workspace_size(...) bytes, 16-byte aligned:
- *               G_i = dO_i . o_i and delta_i (fp32 per query row), then, used by
- *               the bf16 path, fp16 copies of q, rho, dO ([B, Hq, T, d]) and
- *               k ([B, Hkv, T, d]) that the kernels stage as MFMA operands
+ *               G_i and delta_i (fp32 per query row); the dO scale (below) and
+ *               the partial maxima it is reduced from; then, used by the bf16
+ *               path, fp16 copies of q, rho, s dO ([B, Hq, T, d]) and k
+ *               ([B, Hkv, T, d]) that the kernels stage as MFMA operands
+ * bf16 path: q, rho, k and v enter fp16 MFMAs (exact for 2^-14 <= |x| <= 65504;
+ * smaller magnitudes keep an absolute error of at most 2^-25, larger ones are
+ * out of range).  dO enters them scaled by the power of two s with
+ * s max|dO| in [1, 2), and the four gradients are multiplied by 1/s as they
+ * are stored, so any dO whose gradients fit fp32 (a loss averaged over
+ * millions of tokens included) keeps full precision: scaling dO by a power of
+ * two scales every gradient by exactly that factor.
  * The result is deterministic (no atomics): one kernel owns each key block and
  * one kernel owns each query block.
  */

@@ -151,8 +151,9 @@ plx_status plx_decode_noalloc(const void* q, const void* rho, const void* k_cach
 size_t plx_bwd_workspace_size(int B, int Hq, int Hkv, int T, int d) {
   if (B < 1 || Hq < 1 || Hkv < 1 || T < 1) return 0;
   if (!dim_ok(d)) return 0;
-  // G_i = dO_i . o_i and delta_i = dO_i . vbar_i (fp32 each), then the fp16
-  // copies of q, rho, dO, k and v that the bf16 path's kernels read
+  // G_i = dO_i . o_i and delta_i = dO_i . vbar_i (fp32 each), the dO scale
+  // and its partial maxima, then the fp16 copies of q, rho, s dO and k that
+  // the bf16 path's kernels read
   return plx::bwd_workspace_bytes(B, Hq, Hkv, T, d);
 }
 

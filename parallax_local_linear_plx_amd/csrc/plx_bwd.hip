@@ -406,7 +406,23 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv_kernel(
 // fp16 operands let one row-major LDS tile serve both the score GEMMs (rows
 // read with ds_read_b128) and the gradient GEMMs (transpose reads,
 // ds_read_b64_tr_b16).  A conversion pass writes the fp16 copies once.
+//
+// Every gradient is linear in dO, and so are the fp16 operands formed from it
+// (dO itself, dS, dR).  An upstream gradient far from unit scale (a loss
+// averaged over many tokens gives |dO| ~ 1e-6) would put them on fp16's
+// subnormal grid, or past its largest value.  The kernels therefore run on
+// s dO, with s the power of two that brings max |dO| into [1, 2), and
+// multiply the four gradients by 1 / s as they store them.  Both scalings are
+// exact, so the result does not depend on the scale of dO except through
+// fp32 underflow or overflow of the gradients themselves.
 inline size_t bwd_ws_align(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workgroups of the preparation pass: each reduces its part of dO to one
+// partial maximum, which bounds the partials buffer in the workspace.
+constexpr int kPrepBlocks = 2048;
+inline size_t bwd_head_bytes(size_t rows) {
+  return bwd_ws_align(2 * rows * sizeof(float)) + bwd_ws_align((4 + kPrepBlocks) * sizeof(unsigned));
+}
 
 __device__ __forceinline__ f16x8 cvt_bf16x8_f16(u32x4 raw) {
   const u16x8 b = __builtin_bit_cast(u16x8, raw);
@@ -416,13 +432,54 @@ __device__ __forceinline__ f16x8 cvt_bf16x8_f16(u32x4 raw) {
   return h;
 }
 
-// bf16 -> fp16 copy of n8 chunks of 8 elements: the dQ kernel stages its K
-// tiles from this copy, so a tile read by every query block of a head is not
-// converted again by each of them.
-__global__ __launch_bounds__(256) void cvt_f16_kernel(const u32x4* __restrict__ src, f16x8* __restrict__ dst,
-                                                     long long n8) {
-  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long long)gridDim.x * 256)
-    dst[i] = cvt_bf16x8_f16(src[i]);
+// Preparation pass, one grid-stride sweep per tensor:
+//  - bf16 -> fp16 copy of K (nk8 chunks of 8 elements): the dQ kernel stages
+//    its K tiles from this copy, so a tile read by every query block of a head
+//    is not converted again by each of them;
+//  - the largest |dO| of this workgroup's chunks (ng8 of them), as bf16 bits
+//    (for non-negative bf16 values the bit patterns order as the values do).
+__global__ __launch_bounds__(256) void bwd_prep16_kernel(const u32x4* __restrict__ k,
+                                                        f16x8* __restrict__ k16, long long nk8,
+                                                        const u32x4* __restrict__ d_o, long long ng8,
+                                                        unsigned* __restrict__ part) {
+  const long long stride = (long long)gridDim.x * 256;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < nk8; i += stride)
+    k16[i] = cvt_bf16x8_f16(k[i]);
+  unsigned m = 0;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < ng8; i += stride) {
+    const u32x4 x = d_o[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = max(m, max(x[e] & 0x7fffu, (x[e] >> 16) & 0x7fffu));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off, 64));
+  __shared__ unsigned wm[4];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
+}
+
+// One workgroup: the largest of the n partial maxima gives the dO scale s (a
+// power of two with s max|dO| in [1, 2)) and its inverse, written to sc[0..1].
+// An all-zero dO, or one holding an infinity or NaN, keeps s = 1.
+__global__ __launch_bounds__(256) void bwd_scale_kernel(const unsigned* __restrict__ part, int n,
+                                                       float* __restrict__ sc) {
+  unsigned m = 0;
+  for (int i = threadIdx.x; i < n; i += 256) m = max(m, part[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off, 64));
+  __shared__ unsigned wm[4];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
+    // biased exponent of max|dO| (bf16 shares fp32's 8-bit exponent)
+    const int ex = (int)(m >> 7);
+    int e2 = 0;
+    if (m != 0 && ex < 255) e2 = min(126, max(-126, 127 - max(ex, 1)));
+    sc[0] = __builtin_ldexpf(1.f, e2);
+    sc[1] = __builtin_ldexpf(1.f, -e2);
+  }
 }
 
 // dQ and drho on 16x16x32 MFMA tiles, two waves per SIMD (bf16 inputs).  The
@@ -457,8 +514,9 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
     const uint16_t* __restrict__ rho, const uint16_t* __restrict__ d_o, const float* __restrict__ o,
     const float* __restrict__ vbar, const float* __restrict__ lse, const float* __restrict__ c_aux,
     float* __restrict__ Gv, float* __restrict__ dlt, _Float16* __restrict__ q16,
-    _Float16* __restrict__ r16, _Float16* __restrict__ g16, float* __restrict__ dq,
-    float* __restrict__ drho, int B, int Hq, int Hkv, int T, float scale, float scale_log2) {
+    _Float16* __restrict__ r16, _Float16* __restrict__ g16, const float* __restrict__ dsc,
+    float* __restrict__ dq, float* __restrict__ drho, int B, int Hq, int Hkv, int T, float scale,
+    float scale_log2) {
   constexpr int NT = 64 * NW, BR = 16 * NW;
   constexpr int NS = D / 32, ND = D / 16, CPR = D / 8;
   constexpr int NCH = BC * CPR / NT;  // 16-byte chunks per thread per tile and tensor
@@ -510,6 +568,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
   };
 
   gload(0);
+  // dO scale s and 1 / s (powers of two, from the preparation pass)
+  const float gsc = dsc[0], ginv = dsc[1];
   // this lane's quarter of its query row: elements 32 s + 8 g .. + 8
   f16x8 qop[NS], rop[NS];
   bf16x8 gop[NS];
@@ -522,6 +582,13 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
       qa = *reinterpret_cast<const u32x4*>(q + off);
       ra = *reinterpret_cast<const u32x4*>(rho + off);
       ga = *reinterpret_cast<const u32x4*>(d_o + off);
+      // s dO is exact in bf16 (a power of two moves only the exponent)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __builtin_bit_cast(float, ga[e] << 16) * gsc;
+        const float hi = __builtin_bit_cast(float, ga[e] & 0xffff0000u) * gsc;
+        ga[e] = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xffff0000u);
+      }
       const f32x4 o0 = *reinterpret_cast<const f32x4*>(o + off);
       const f32x4 o1 = *reinterpret_cast<const f32x4*>(o + off + 4);
       const f32x4 v0 = *reinterpret_cast<const f32x4*>(vbar + off);
@@ -567,7 +634,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
     dra[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  auto subtile = [&](int buf, int st, int kbase, auto masked) {
+  auto subtile = [&](int buf, int st, int kbase) {
     // scores S^T, R^T and A^T = V dO^T for 32 keys
     unsigned kaddr = lds_addr(&sm.k[buf][(32 * st + c) * SM::LD + 8 * g]);
     unsigned vaddr = lds_addr(&sm.v[buf][(32 * st + c) * SM::LD + 8 * g]);
@@ -604,14 +671,22 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
       kt[dt] = __builtin_shufflevector(tr16_at(taddr + 2 * 16 * dt),
                                        tr16_at(taddr + 2 * (16 * dt + 16 * SM::LD)), 0, 1, 2, 3, 4, 5, 6, 7);
     __builtin_amdgcn_sched_barrier(0);
+    // causal mask where the sub-tile reaches past the wave's first query (a
+    // uniform branch: one code path for every sub-tile, so the accumulators
+    // stay in place instead of being copied where two variants would join)
+    if (kbase + 31 > qw) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (kbase + 16 * t + 4 * g + j > my_q) sacc[t][j] = -INFINITY;
+    }
     // dS^T, dR^T: element e of group g is key 16 (e / 4) + 4 g + e % 4, query c
     f16x8 dsop, drop;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int t = e >> 2, j = e & 3;
-      float p = fast_exp2(__builtin_fmaf(sacc[t][j], scale_log2, -lse2));
-      if constexpr (decltype(masked)::value)
-        if (kbase + 16 * t + 4 * g + j > my_q) p = 0.f;
+      const float p = fast_exp2(__builtin_fmaf(sacc[t][j], scale_log2, -lse2));
       const float r = racc[t][j], A = aacc[t][j];
       const float tt = di - A;
       dsop[e] = (_Float16)(p * __builtin_fmaf(A, k1, __builtin_fmaf(r, tt, -k2)));
@@ -632,12 +707,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
 #pragma unroll
     for (int st = 0; st < BC / 32; ++st) {
       const int kbase = key0 + 32 * st;
-      if ((BC / 32) * j + st < nsub) {
-        if (kbase + 31 > qw)
-          subtile(buf, st, kbase, std::true_type{});
-        else
-          subtile(buf, st, kbase, std::false_type{});
-      }
+      if ((BC / 32) * j + st < nsub) subtile(buf, st, kbase);
     }
     if (j + 1 < ntiles) lds_put(buf ^ 1);
     __syncthreads();
@@ -656,8 +726,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
       f32x4 x, y;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        x[jj] = scale * dqa[dt][jj];
-        y[jj] = dra[dt][jj];
+        x[jj] = (scale * ginv) * dqa[dt][jj];
+        y[jj] = ginv * dra[dt][jj];
       }
       *reinterpret_cast<f32x4*>(dqr + 16 * dt + 4 * g) = x;
       *reinterpret_cast<f32x4*>(drr + 16 * dt + 4 * g) = y;
@@ -682,7 +752,7 @@ struct DkbSmem {
   alignas(16) _Float16 q[2][BQ * LD];
   alignas(16) _Float16 r[2][BQ * LD];
   alignas(16) _Float16 g[2][BQ * LD];
-  alignas(16) float sc[2][4][BQ];  // per query row: lse * log2e, 1 + c, G + delta c, delta
+  alignas(16) float sc[2][BQ][4];  // per query row: lse * log2e, 1 + c, G + delta c, delta
 };
 
 template <int D, int NW, int BQ>
@@ -690,8 +760,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ rho, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
     const float* __restrict__ c_aux, const float* __restrict__ Gv, const float* __restrict__ dlt,
-    float* __restrict__ dk, float* __restrict__ dv, int B, int Hq, int Hkv, int T, float scale,
-    float scale_log2) {
+    const float* __restrict__ dsc, float* __restrict__ dk, float* __restrict__ dv, int B, int Hq,
+    int Hkv, int T, float scale, float scale_log2) {
   constexpr int NT = 64 * NW, BK = 16 * NW;
   constexpr int NS = D / 32, ND = D / 16, CPR = D / 8;
   constexpr int NCH = BQ * CPR / NT;  // 16-byte chunks per thread per tile and tensor
@@ -712,6 +782,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
   const bool kvalid = my_k < T;
 
   const size_t kvbase = (size_t)bhk * T;
+  const float ginv = dsc[1];  // 1 / s of the dO scale
   const int nqt = (T - k0 + BQ - 1) / BQ;  // query tiles per head (queries >= k0)
   const int ntile = G * nqt;
 
@@ -761,12 +832,9 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
       *reinterpret_cast<u32x4*>(&sm.r[buf][o]) = pr[i];
       *reinterpret_cast<u32x4*>(&sm.g[buf][o]) = pg[i];
     }
-    if (threadIdx.x < BQ) {
-      sm.sc[buf][0][threadIdx.x] = psc[0] * kLog2e;
-      sm.sc[buf][1][threadIdx.x] = 1.f + psc[1];
-      sm.sc[buf][2][threadIdx.x] = psc[2] + psc[3] * psc[1];
-      sm.sc[buf][3][threadIdx.x] = psc[3];
-    }
+    if (threadIdx.x < BQ)
+      *reinterpret_cast<f32x4*>(&sm.sc[buf][threadIdx.x][0]) =
+          (f32x4){psc[0] * kLog2e, 1.f + psc[1], psc[2] + psc[3] * psc[1], psc[3]};
   };
 
   gload(0);
@@ -793,7 +861,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
   }
 
   // one 32-query sub-tile st of the tile in buffer buf (first query qs)
-  auto subtile = [&](int buf, int st, int qs, auto masked) {
+  auto subtile = [&](int buf, int st, int qs) {
     f32x4 sacc[2], racc[2], aacc[2];
     {
       unsigned qa = lds_addr(&sm.q[buf][(32 * st + c) * SM::LD + 8 * g]);
@@ -824,28 +892,34 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
       }
     }
     // accumulator element j of key tile t: query qs + 16 t + 4 g + j, key c;
-    // the same order as the K index of the transpose-read A operands below
+    // the same order as the K index of the transpose-read A operands below.
+    // Causal mask (queries before the key) and rows past T, in a uniform
+    // branch: one code path for every sub-tile (see the dQ kernel).
+    if (qs < kw + 15 || qs + 31 >= T) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int qi = qs + 16 * t + 4 * g + j;
+          if (qi < my_k || qi >= T) sacc[t][j] = -INFINITY;
+        }
+    }
     f16x8 pop, dsop, drop;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int r0 = 32 * st + 16 * t + 4 * g;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.sc[buf][0][r0]);
-      const f32x4 k14 = *reinterpret_cast<const f32x4*>(&sm.sc[buf][1][r0]);
-      const f32x4 k24 = *reinterpret_cast<const f32x4*>(&sm.sc[buf][2][r0]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.sc[buf][3][r0]);
+      f32x4 rs[4];  // lse * log2e, 1 + c, G + delta c, delta of query r0 + j
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rs[j] = *reinterpret_cast<const f32x4*>(&sm.sc[buf][r0 + j][0]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float p = fast_exp2(__builtin_fmaf(sacc[t][j], scale_log2, -l4[j]));
-        if constexpr (decltype(masked)::value) {
-          const int qi = qs + 16 * t + 4 * g + j;
-          if (qi < my_k || qi >= T) p = 0.f;
-        }
+        const float p = fast_exp2(__builtin_fmaf(sacc[t][j], scale_log2, -rs[j][0]));
         const float r = racc[t][j], A = aacc[t][j];
         // with f = 1 + c - r:  dS = p [f A + delta r - (G + delta c)],  dR = p (delta - A)
-        const float f = k14[j] - r;
+        const float f = rs[j][1] - r;
         pop[4 * t + j] = (_Float16)(p * f);
-        dsop[4 * t + j] = (_Float16)((scale * p) * __builtin_fmaf(A, f, __builtin_fmaf(r, d4[j], -k24[j])));
-        drop[4 * t + j] = (_Float16)(p * (d4[j] - A));
+        dsop[4 * t + j] = (_Float16)((scale * p) * __builtin_fmaf(A, f, __builtin_fmaf(r, rs[j][3], -rs[j][2])));
+        drop[4 * t + j] = (_Float16)(p * (rs[j][3] - A));
       }
     }
     // gradient MFMAs: A = Q^T / rho^T / dO^T, 16 d rows x 32 queries each
@@ -875,10 +949,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
     for (int st = 0; st < BQ / 32; ++st) {
       const int qs = qt0 + 32 * st;
       if (qs + 31 < kw) continue;  // every query of the sub-tile precedes every key of the wave
-      if (qs < kw + 15 || qs + 31 >= T)
-        subtile(buf, st, qs, std::true_type{});
-      else
-        subtile(buf, st, qs, std::false_type{});
+      subtile(buf, st, qs);
     }
     if (n + 1 < ntile) lds_put(buf ^ 1);  // buffer last read in iteration n-1
     __syncthreads();
@@ -888,7 +959,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
     if (n + 1 < ntile) iter(n + 1, 1);
   }
 
-  // dka[dt][jj] is d = 16 dt + 4 g + jj of key c
+  // dka[dt][jj] is d = 16 dt + 4 g + jj of key c; the sums ran on s dO
   if (kvalid) {
     float* dkr = dk + (kvbase + my_k) * D;
     float* dvr = dv + (kvbase + my_k) * D;
@@ -897,8 +968,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
       f32x4 x, y;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        x[jj] = dka[dt][jj];
-        y[jj] = dva[dt][jj];
+        x[jj] = ginv * dka[dt][jj];
+        y[jj] = ginv * dva[dt][jj];
       }
       *reinterpret_cast<f32x4*>(dkr + 16 * dt + 4 * g) = x;
       *reinterpret_cast<f32x4*>(dvr + 16 * dt + 4 * g) = y;
@@ -922,15 +993,20 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
     // workspace after G and delta: fp16 copies of q, rho, dO (written by the
     // dQ kernel) and of K (written by the conversion pass)
     const size_t nq = (size_t)rows * D, nk = (size_t)B * Hkv * T * D;
-    _Float16* q16 = (_Float16*)((char*)ws + bwd_ws_align(2 * rows * sizeof(float)));
+    float* dsc = (float*)((char*)ws + bwd_ws_align(2 * rows * sizeof(float)));
+    unsigned* part = (unsigned*)(dsc + 4);
+    _Float16* q16 = (_Float16*)((char*)ws + bwd_head_bytes(rows));
     _Float16* r16 = q16 + nq;
     _Float16* g16 = r16 + nq;
     _Float16* k16 = g16 + nq;
     {
-      const long long n8 = (long long)nk / 8;
-      const unsigned blocks = (unsigned)std::min<long long>((n8 + 255) / 256, 8192);
-      hipLaunchKernelGGL(cvt_f16_kernel, dim3(blocks), dim3(256), 0, stream, (const u32x4*)k,
-                         (f16x8*)k16, n8);
+      const long long nk8 = (long long)nk / 8, ng8 = (long long)nq / 8;
+      const unsigned blocks = (unsigned)std::min<long long>((std::max(nk8, ng8) + 255) / 256, kPrepBlocks);
+      hipLaunchKernelGGL(bwd_prep16_kernel, dim3(blocks), dim3(256), 0, stream, (const u32x4*)k,
+                         (f16x8*)k16, nk8, (const u32x4*)d_o, ng8, part);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL(bwd_scale_kernel, dim3(1), dim3(256), 0, stream, (const unsigned*)part,
+                         (int)blocks, dsc);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // waves per workgroup and tile sizes: see DqbSmem
@@ -940,12 +1016,12 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
     hipLaunchKernelGGL((bwd_dq16b_kernel<D, NW, BC>), dim3(nqb16 * B * Hq), dim3(64 * NW), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k16, (const uint16_t*)v,
                        (const uint16_t*)rho, (const uint16_t*)d_o, o, vbar, lse, c_aux, G, dl, q16,
-                       r16, g16, dq, drho, B, Hq, Hkv, T, scale, scale * kLog2e);
+                       r16, g16, dsc, dq, drho, B, Hq, Hkv, T, scale, scale * kLog2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv16b_kernel<D, NW, BQ>), dim3(nkb16 * B * Hkv), dim3(64 * NW), 0, stream,
                        (const uint16_t*)q16, (const uint16_t*)k, (const uint16_t*)v,
-                       (const uint16_t*)r16, (const uint16_t*)g16, lse, c_aux, G, dl, dk, dv, B, Hq,
-                       Hkv, T, scale, scale * kLog2e);
+                       (const uint16_t*)r16, (const uint16_t*)g16, lse, c_aux, G, dl, dsc, dk, dv, B,
+                       Hq, Hkv, T, scale, scale * kLog2e);
     return hipGetLastError();
   } else {
     hipLaunchKernelGGL((bwd_pre_kernel<Pol, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
@@ -967,12 +1043,12 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
 
 }  // namespace
 
-// Workspace of the backward: G and delta (fp32 per query row), then, for bf16
+// Workspace of the backward: G and delta (fp32 per query row); the dO scale,
+// its inverse and the preparation pass's partial maxima; then, for bf16
 // inputs, fp16 copies of q, rho, dO ([B, Hq, T, d]) and K ([B, Hkv, T, d]).
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int T, int d) {
   const size_t rows = (size_t)B * Hq * T;
-  return bwd_ws_align(2 * rows * sizeof(float)) +
-         (3 * rows * d + (size_t)B * Hkv * T * d) * sizeof(uint16_t);
+  return bwd_head_bytes(rows) + (3 * rows * d + (size_t)B * Hkv * T * d) * sizeof(uint16_t);
 }
 
 hipError_t launch_bwd(int dtype, const void* q, const void* k, const void* v, const void* rho,

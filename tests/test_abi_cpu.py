@@ -169,14 +169,13 @@ def test_balanced_decode_workspace_follows_the_schedule(B, Hq, Hkv, S_max, d):
 
 
 def test_bwd_workspace_size():
-    # G and delta (fp32 per query row, padded to 256 bytes), then fp16 copies of
-    # q, rho, dO ([B, Hq, T, d]) and k, v ([B, Hkv, T, d])
-    B, Hq, Hkv, T, d = 8, 16, 8, 4096, 128
-    head = (2 * B * Hq * T * 4 + 255) // 256 * 256
-    assert binding.bwd_workspace_size(B, Hq, Hkv, T, d) == head + (3 * B * Hq * T * d + B * Hkv * T * d) * 2
-    B, Hq, Hkv, T, d = 1, 2, 1, 3, 64
-    head = (2 * B * Hq * T * 4 + 255) // 256 * 256
-    assert binding.bwd_workspace_size(B, Hq, Hkv, T, d) == head + (3 * B * Hq * T * d + B * Hkv * T * d) * 2
+    # G and delta (fp32 per query row, padded to 256 bytes); the dO scale, its
+    # inverse and 2048 partial maxima (4 + 2048 words, padded to 256 bytes);
+    # then fp16 copies of q, rho, dO ([B, Hq, T, d]) and k ([B, Hkv, T, d])
+    for B, Hq, Hkv, T, d in ((8, 16, 8, 4096, 128), (1, 2, 1, 3, 64), (2, 16, 1, 300, 256)):
+        head = (2 * B * Hq * T * 4 + 255) // 256 * 256 + (4 * (4 + 2048) + 255) // 256 * 256
+        want = head + (3 * B * Hq * T * d + B * Hkv * T * d) * 2
+        assert binding.bwd_workspace_size(B, Hq, Hkv, T, d) == want
     assert binding.bwd_workspace_size(8, 16, 8, 0, 128) == 0
 
 

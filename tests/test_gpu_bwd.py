@@ -11,12 +11,14 @@ from tests._util import check_bf16, check_fp32_grad, say, to_device
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl):
+def _run(wl, do_scale=1.0):
     import torch
 
     from parallax_local_linear_plx_amd import plx_bwd, plx_fwd_prefill
 
     t = {n: to_device(x) for n, x in wl.tensors.items()}
+    if do_scale != 1.0:
+        t["d_o"] = t["d_o"] * do_scale  # a power of two: exact in the input dtype
     fwd = plx_fwd_prefill(t["q"], t["k"], t["v"], t["rho"], wl.scale, aux=True)
     nan = float("nan")
     grads = {
@@ -99,6 +101,24 @@ def test_bf16_gradients_projected_probe_scale(gpu_lib, T):
     ref = _oracle(wl)
     for n in ("dq", "dk", "dv", "drho"):
         check_bf16(got[n], ref[n], n)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_bf16_gradients_follow_the_scale_of_do(gpu_lib, d):
+    """Every gradient is linear in dO.  dO x 2^-20 (the size of a loss averaged
+    over about a million tokens, far below fp16's normal range) and dO x 2^12
+    give exactly the unscaled run's gradients times 2^-20 and 2^12, and, back at
+    unit scale, they meet the bf16 bars against the oracle."""
+    B, Hq, Hkv, T = (1, 4, 2, 300) if d < 256 else (1, 4, 1, 129)
+    say(f"case bwd bf16 dO scale B{B} Hq{Hq} Hkv{Hkv} T{T} d{d}")
+    wl = inputs.make_prefill(B, Hq, Hkv, T, d, dtype="bf16", seed=700 + d, with_grad=True)
+    base = _run(wl)
+    ref = _oracle(wl)
+    for e in (-20, 12):
+        got = _run(wl, do_scale=2.0 ** e)
+        for n in ("dq", "dk", "dv", "drho"):
+            np.testing.assert_array_equal(got[n], base[n] * np.float32(2.0 ** e), err_msg=f"{n} at 2^{e}")
+            check_bf16(got[n] * np.float32(2.0 ** -e), ref[n], f"{n} at 2^{e}")
 
 
 def test_zero_probe_gradients_are_attention_gradients(gpu_lib):
