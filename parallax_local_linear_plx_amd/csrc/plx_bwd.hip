@@ -549,6 +549,18 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
   // and masked by the causal test since they follow every query)
   u32x4 pk[NCH], pv[NCH];
   auto gload = [&](int key0) {
+    if (key0 + BC <= T) {
+      // whole tile in range: a uniform tile base plus this thread's fixed offsets
+      const uint16_t* kt = kp + (size_t)key0 * D;
+      const uint16_t* vt = vp + (size_t)key0 * D;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int off = (threadIdx.x + NT * i) * 8;  // row * D + column
+        pk[i] = *reinterpret_cast<const u32x4*>(kt + off);
+        pv[i] = *reinterpret_cast<const u32x4*>(vt + off);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int it = threadIdx.x + NT * i;
@@ -807,6 +819,25 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
     size_t rowbase;
     int qt0;
     tile_rows(n, rowbase, qt0);
+    if (threadIdx.x < BQ) {
+      const size_t r = rowbase + min(qt0 + (int)threadIdx.x, T - 1);
+      psc[0] = lse[r];
+      psc[1] = c_aux[r];
+      psc[2] = Gv[r];
+      psc[3] = dlt[r];
+    }
+    if (qt0 + BQ <= T) {
+      // whole tile in range: a uniform tile base plus this thread's fixed offsets
+      const size_t tb = (rowbase + qt0) * D;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int off = (threadIdx.x + NT * i) * 8;  // row * D + column
+        pq[i] = *reinterpret_cast<const u32x4*>(q + tb + off);
+        pr[i] = *reinterpret_cast<const u32x4*>(rho + tb + off);
+        pg[i] = *reinterpret_cast<const u32x4*>(d_o + tb + off);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int it = threadIdx.x + NT * i;
@@ -814,13 +845,6 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
       pq[i] = *reinterpret_cast<const u32x4*>(q + off);
       pr[i] = *reinterpret_cast<const u32x4*>(rho + off);
       pg[i] = *reinterpret_cast<const u32x4*>(d_o + off);
-    }
-    if (threadIdx.x < BQ) {
-      const size_t r = rowbase + min(qt0 + (int)threadIdx.x, T - 1);
-      psc[0] = lse[r];
-      psc[1] = c_aux[r];
-      psc[2] = Gv[r];
-      psc[3] = dlt[r];
     }
   };
   auto lds_put = [&](int buf) {
