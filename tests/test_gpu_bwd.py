@@ -139,6 +139,17 @@ def test_zero_probe_gradients_are_attention_gradients(gpu_lib):
         check_fp32_grad(got[n], ref, mag[n], _n_terms(wl), n)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_upstream_gradient_gives_zero_gradients(gpu_lib, dtype):
+    """dO = 0: every gradient is exactly zero (the bf16 path keeps its dO
+    scale at 1 when max|dO| = 0, so nothing is divided by zero)."""
+    wl = inputs.make_prefill(1, 4, 2, 150, 64, dtype=dtype, seed=302, with_grad=True)
+    wl.tensors["d_o"].data[...] = 0
+    got = _run(wl)
+    for n in got:
+        assert np.all(got[n] == 0), n
+
+
 def test_repeat_runs_are_bitwise_identical(gpu_lib):
     wl = inputs.make_prefill(1, 2, 1, 260, 128, dtype="bf16", seed=301, with_grad=True)
     a = _run(wl)
