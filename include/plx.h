@@ -144,8 +144,9 @@ plx_status plx_fwd_prefill(const void* q, const void* k, const void* v, const vo
  *   num_splits    0 = automatic (see above), else the number of key splits over S_max
  *   workspace     device scratch of at least plx_decode_workspace_size(...) bytes,
  *                 16-byte aligned; contents on entry are ignored
- * Requires group = Hq / Hkv in {1, 2, 4, 8, 16}.  Rows of the cache at or beyond
- * ctx_len[b] are never read.  The result is deterministic (no atomics; the
+ * Any group size Hq / Hkv: up to 16 query heads of a KV head share one pass
+ * over its cache; larger groups take one pass per 16 heads.  Rows of the cache
+ * at or beyond ctx_len[b] are never read.  The result is deterministic (no atomics; the
  * waves of a workgroup and the records of a head are combined in fixed order).
  */
 size_t plx_decode_workspace_size(int B, int Hq, int Hkv, int S_max, int d, int num_splits);

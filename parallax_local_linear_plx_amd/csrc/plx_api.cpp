@@ -102,8 +102,6 @@ static plx_status check_decode(const void* q, const void* rho, const void* k_cac
     return PLX_ERR_INVALID_ARG;
   plx_status st = check_heads(B, Hq, Hkv, d, dtype, true);
   if (st != PLX_OK) return st;
-  const int group = Hq / Hkv;
-  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16) return PLX_ERR_UNSUPPORTED;
   if (!size_ok((long long)B * Hkv * S_max, d)) return PLX_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(rho) || !aligned16(k_cache) || !aligned16(v_cache) ||
       !aligned16(o) || !aligned4(ctx_len) || !aligned4(lse) || !aligned4(cor))

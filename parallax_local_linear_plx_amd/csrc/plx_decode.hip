@@ -61,12 +61,14 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <class Pol, int D, int G>
+// The launch covers the nh <= 16 heads hoff .. hoff+nh-1 of every KV head's
+// group of Hq / Hkv (2 nh of the 32 B-operand columns).
+template <class Pol, int D>
 __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
     const typename Pol::in_t* __restrict__ q, const typename Pol::in_t* __restrict__ rho,
     const typename Pol::in_t* __restrict__ kc, const typename Pol::in_t* __restrict__ vc,
-    const int32_t* __restrict__ ctx_len, float* __restrict__ part, int Hkv, int S_max, int chunk,
-    int nsplit, unsigned flags, float scale_log2) {
+    const int32_t* __restrict__ ctx_len, float* __restrict__ part, int Hq, int Hkv, int S_max,
+    int chunk, int nsplit, int hoff, int nh, unsigned flags, float scale_log2) {
   using in_t = typename Pol::in_t;
   using sop_t = typename Pol::sop_t;
   using vop_t = typename Pol::vop_t;
@@ -88,15 +90,15 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 31, half = lane >> 5;
-  const int Hq = Hkv * G;
+  const int hq0 = hk * (Hq / Hkv) + hoff;  // first query head of this launch's share
 
-  // B operand: column c -> q (even) or rho (odd) of head hk*G + c/2; with
+  // B operand: column c -> q (even) or rho (odd) of head hq0 + c/2; with
   // uniform weights the q columns are zero (every score exactly 0, p = 1)
   sop_t bop[NS];
   {
-    const int hq = hk * G + (col >> 1);
+    const int hq = hq0 + (col >> 1);
     const in_t* src = (col & 1) ? rho : q;
-    const bool load = col < 2 * G && ((col & 1) || !(flags & PLX_UNIFORM_WEIGHTS));
+    const bool load = col < 2 * nh && ((col & 1) || !(flags & PLX_UNIFORM_WEIGHTS));
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       bop[s] = load ? load_sop<Pol>(src + ((size_t)b * Hq + hq) * D + KSTEP * s + KW * half)
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
     m_run = m_new;
-    const bool used = col < 2 * G;
+    const bool used = col < 2 * nh;
     const bool odd = col & 1;
     float lsum = 0.f, esum = 0.f;
 #pragma unroll
@@ -230,8 +232,8 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_partial_kernel(
 
   // record of head g: [m, l, e, C, O[D], U[D]]  (m in log2 units; l the
   // rounded-operand sum, e the unrounded sum; C the odd column's rounded sum)
-  for (int g = 0; g < G; ++g) {
-    float* rec = part + (((size_t)b * Hq + hk * G + g) * nsplit + split) * REC;
+  for (int g = 0; g < nh; ++g) {
+    float* rec = part + (((size_t)b * Hq + hq0 + g) * nsplit + split) * REC;
     const int c0 = 2 * g;
     if (threadIdx.x == 0) {
       float M0 = -INFINITY, l0 = 0.f, e0 = 0.f, C0 = 0.f;
@@ -360,12 +362,13 @@ __device__ long long bal_total(const int32_t* __restrict__ ctx_len, int B, int H
   return s * Hkv;
 }
 
-// One workgroup's pass over keys [k_begin, k_end) of (b, hk) for the G heads
-// hq0 .. hq0+G-1; writes record hh at rec + hh * rec_stride:
+// One workgroup's pass over keys [k_begin, k_end) of (b, hk) for the nh <= G
+// heads hq0 .. hq0+nh-1 (G: the column capacity in heads); writes record hh
+// at rec + hh * rec_stride:
 //   [m (log2 units), l, e, C, O[D], U[D]].
 // G = 16 takes two column groups: both B operands are multiplied by every K
-// operand and both sets of value MFMAs share every V operand, so the sixteen
-// heads of a KV head still read its cache once.
+// operand and both sets of value MFMAs share every V operand, so up to sixteen
+// heads of a KV head read its cache once.
 template <int D, int G>
 __device__ __forceinline__ void dec16_range(Dec16Smem<D, (G > 8 ? 2 : 1)>& sm,
                                             const uint16_t* __restrict__ q,
@@ -373,8 +376,8 @@ __device__ __forceinline__ void dec16_range(Dec16Smem<D, (G > 8 ? 2 : 1)>& sm,
                                             const uint16_t* __restrict__ kc,
                                             const uint16_t* __restrict__ vc, int b, int hk, int hq0,
                                             int Hq, int Hkv, int S_max, int k_begin, int k_end,
-                                            unsigned flags, float scale_log2, float* __restrict__ rec,
-                                            size_t rec_stride) {
+                                            int nh, unsigned flags, float scale_log2,
+                                            float* __restrict__ rec, size_t rec_stride) {
   constexpr int NS = D / 32;  // 32-deep score steps
   constexpr int ND = D / 16;  // 16-row d tiles of the value accumulators
   constexpr int NCG = G > 8 ? 2 : 1;  // column groups of 16 (8 heads each)
@@ -392,7 +395,7 @@ __device__ __forceinline__ void dec16_range(Dec16Smem<D, (G > 8 ? 2 : 1)>& sm,
     const int cg = i / (16 * D / 8), cc = (i / (D / 8)) % 16, d0 = (i % (D / 8)) * 8;
     const int head = 8 * cg + (cc >> 1);
     u32x4 raw = {0u, 0u, 0u, 0u};
-    if (head < G && ((cc & 1) || use_q)) {
+    if (head < nh && ((cc & 1) || use_q)) {
       const uint16_t* src = (cc & 1) ? rho : q;
       raw = *reinterpret_cast<const u32x4*>(src + ((size_t)b * Hq + hq0 + head) * D + d0);
     }
@@ -412,7 +415,7 @@ __device__ __forceinline__ void dec16_range(Dec16Smem<D, (G > 8 ? 2 : 1)>& sm,
     for (int i = 0; i < ND; ++i) ou[cg][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
     m_run[cg] = -INFINITY;
     l_part[cg] = e_part[cg] = 0.f;
-    used[cg] = 8 * cg + (c >> 1) < G;
+    used[cg] = 8 * cg + (c >> 1) < nh;
   }
   const bool odd = c & 1;
 
@@ -574,7 +577,7 @@ __device__ __forceinline__ void dec16_range(Dec16Smem<D, (G > 8 ? 2 : 1)>& sm,
       }
     __syncthreads();
 
-    for (int hl = 0; hl < 8 && 8 * cg + hl < G; ++hl) {
+    for (int hl = 0; hl < 8 && 8 * cg + hl < nh; ++hl) {
       float* r = rec + (8 * cg + hl) * rec_stride;
       const int c0 = 2 * hl;
       if (threadIdx.x == 0) {
@@ -609,7 +612,8 @@ template <int D, int G>
 __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_chunk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ rho, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ ctx_len, float* __restrict__ part,
-    int Hq, int Hkv, int S_max, int chunk, int nsplit, int hoff, unsigned flags, float scale_log2) {
+    int Hq, int Hkv, int S_max, int chunk, int nsplit, int hoff, int nh, unsigned flags,
+    float scale_log2) {
   constexpr int REC = 2 * D + 4;
   __shared__ Dec16Smem<D, (G > 8 ? 2 : 1)> sm;
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -619,7 +623,7 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_chunk_kernel(
   const int k_end = min(ctx, k_begin + chunk);
   const int hq0 = hk * (Hq / Hkv) + hoff;
   float* rec = part + (((size_t)b * Hq + hq0) * nsplit + split) * REC;
-  dec16_range<D, G>(sm, q, rho, kc, vc, b, hk, hq0, Hq, Hkv, S_max, k_begin, k_end, flags,
+  dec16_range<D, G>(sm, q, rho, kc, vc, b, hk, hq0, Hq, Hkv, S_max, k_begin, k_end, nh, flags,
                     scale_log2, rec, (size_t)nsplit * REC);
 }
 
@@ -743,7 +747,7 @@ template <int D, int G>
 __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_balanced_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ rho, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ ctx_len, float* __restrict__ part,
-    int B, int Hq, int Hkv, int S_max, int hoff, unsigned flags, float scale_log2) {
+    int B, int Hq, int Hkv, int S_max, int hoff, int nh, unsigned flags, float scale_log2) {
   constexpr int REC = 2 * D + 4;
   __shared__ Dec16Smem<D, (G > 8 ? 2 : 1)> sm;
   const int lane = threadIdx.x & 63;
@@ -788,8 +792,8 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_balanced_kernel(
     const int hq0 = hk * Gfull + hoff;
     const long long seg = (long long)b * Hkv + hk;
     float* rec = part + ((size_t)(blockIdx.x + seg) * Gfull + hoff) * REC;
-    dec16_range<D, G>(sm, q, rho, kc, vc, b, hk, hq0, Hq, Hkv, S_max, key, k_end, flags, scale_log2,
-                      rec, REC);
+    dec16_range<D, G>(sm, q, rho, kc, vc, b, hk, hq0, Hq, Hkv, S_max, key, k_end, nh, flags,
+                      scale_log2, rec, REC);
     pos += k_end - key;
     if (pos >= hi) break;
     key = 0;
@@ -806,17 +810,17 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode16_balanced_kernel(
 template <int D, int G>
 hipError_t launch_partial16(const void* q, const void* rho, const void* kc, const void* vc,
                             const int32_t* ctx_len, float* part, int B, int Hq, int Hkv, int S_max,
-                            int chunk, int nsplit, int hoff, unsigned flags, float scale,
+                            int chunk, int nsplit, int hoff, int nh, unsigned flags, float scale,
                             hipStream_t stream) {
   if (chunk <= 0) {
     hipLaunchKernelGGL((decode16_balanced_kernel<D, G>), dim3(nsplit), dim3(DEC_THREADS), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)rho, (const uint16_t*)kc, (const uint16_t*)vc,
-                       ctx_len, part, B, Hq, Hkv, S_max, hoff, flags, scale * kLog2e);
+                       ctx_len, part, B, Hq, Hkv, S_max, hoff, nh, flags, scale * kLog2e);
   } else {
     dim3 grid(nsplit, Hkv, B);
     hipLaunchKernelGGL((decode16_chunk_kernel<D, G>), grid, dim3(DEC_THREADS), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)rho, (const uint16_t*)kc, (const uint16_t*)vc,
-                       ctx_len, part, Hq, Hkv, S_max, chunk, nsplit, hoff, flags, scale * kLog2e);
+                       ctx_len, part, Hq, Hkv, S_max, chunk, nsplit, hoff, nh, flags, scale * kLog2e);
   }
   return hipGetLastError();
 }
@@ -895,15 +899,16 @@ __global__ __launch_bounds__(256) void decode_merge_balanced_kernel(const float*
                 flags, orow, lse_out, cor_out);
 }
 
-template <class Pol, int D, int G>
+template <class Pol, int D>
 hipError_t launch_partial(const void* q, const void* rho, const void* kc, const void* vc,
-                          const int32_t* ctx_len, float* part, int B, int Hkv, int S_max, int chunk,
-                          int nsplit, unsigned flags, float scale, hipStream_t stream) {
+                          const int32_t* ctx_len, float* part, int B, int Hq, int Hkv, int S_max,
+                          int chunk, int nsplit, int hoff, int nh, unsigned flags, float scale,
+                          hipStream_t stream) {
   using in_t = typename Pol::in_t;
   dim3 grid(nsplit, Hkv, B);
-  hipLaunchKernelGGL((decode_partial_kernel<Pol, D, G>), grid, dim3(DEC_THREADS), 0, stream,
+  hipLaunchKernelGGL((decode_partial_kernel<Pol, D>), grid, dim3(DEC_THREADS), 0, stream,
                      (const in_t*)q, (const in_t*)rho, (const in_t*)kc, (const in_t*)vc, ctx_len, part,
-                     Hkv, S_max, chunk, nsplit, flags, scale * kLog2e);
+                     Hq, Hkv, S_max, chunk, nsplit, hoff, nh, flags, scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -913,21 +918,29 @@ hipError_t launch_decode_t(const void* q, const void* rho, const void* kc, const
                            unsigned flags, int B, int Hq, int Hkv, int S_max, float scale, int chunk,
                            int nsplit, float* part, hipStream_t stream) {
   const int G = Hq / Hkv;
-  hipError_t e;
+  hipError_t e = hipSuccess;
+  // Every group of G = Hq / Hkv query heads is covered by launches of at most
+  // 16 heads (hoff .. hoff + nh - 1 of each group), each on the smallest
+  // kernel whose column capacity holds nh heads; a group of up to 16 heads
+  // thus reads its KV head's cache once.
+  auto cap_of = [](int nh) { return nh <= 1 ? 1 : nh <= 2 ? 2 : nh <= 4 ? 4 : nh <= 8 ? 8 : 16; };
   if constexpr (sizeof(typename Pol::in_t) == 2) {
-    // bf16: 16-column kernel; 16 heads per KV head take two column groups of
-    // the same launch
-#define PLX_P16(GG, HOFF)                                                                          \
-  launch_partial16<D, GG>(q, rho, kc, vc, ctx_len, part, B, Hq, Hkv, S_max, chunk, nsplit, HOFF, \
-                          flags, scale, stream)
-    switch (G) {
-      case 1: e = PLX_P16(1, 0); break;
-      case 2: e = PLX_P16(2, 0); break;
-      case 4: e = PLX_P16(4, 0); break;
-      case 8: e = PLX_P16(8, 0); break;
-      default: e = PLX_P16(16, 0); break;
-    }
+    // bf16: 16-column kernel; more than 8 heads take two column groups of the
+    // same launch
+    for (int hoff = 0; hoff < G && e == hipSuccess; hoff += 16) {
+      const int nh = min(16, G - hoff);
+#define PLX_P16(GG)                                                                                \
+  launch_partial16<D, GG>(q, rho, kc, vc, ctx_len, part, B, Hq, Hkv, S_max, chunk, nsplit, hoff,  \
+                          nh, flags, scale, stream)
+      switch (cap_of(nh)) {
+        case 1: e = PLX_P16(1); break;
+        case 2: e = PLX_P16(2); break;
+        case 4: e = PLX_P16(4); break;
+        case 8: e = PLX_P16(8); break;
+        default: e = PLX_P16(16); break;
+      }
 #undef PLX_P16
+    }
     if (e != hipSuccess) return e;
     if (chunk <= 0)
       hipLaunchKernelGGL((decode_merge_balanced_kernel<D>), dim3((B * Hq + 3) / 4), dim3(256), 0, stream,
@@ -937,14 +950,11 @@ hipError_t launch_decode_t(const void* q, const void* rho, const void* kc, const
                          part, ctx_len, o, lse, cor, flags, B, Hq, S_max, chunk, nsplit);
     return hipGetLastError();
   } else {
-    // fp32: the generic 32-column kernel (chunked schedule only)
-    switch (G) {
-      case 1: e = launch_partial<Pol, D, 1>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, flags, scale, stream); break;
-      case 2: e = launch_partial<Pol, D, 2>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, flags, scale, stream); break;
-      case 4: e = launch_partial<Pol, D, 4>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, flags, scale, stream); break;
-      case 8: e = launch_partial<Pol, D, 8>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, flags, scale, stream); break;
-      default: e = launch_partial<Pol, D, 16>(q, rho, kc, vc, ctx_len, part, B, Hkv, S_max, chunk, nsplit, flags, scale, stream); break;
-    }
+    // fp32: the generic 32-column kernel (chunked schedule only), up to 16
+    // heads per launch
+    for (int hoff = 0; hoff < G && e == hipSuccess; hoff += 16)
+      e = launch_partial<Pol, D>(q, rho, kc, vc, ctx_len, part, B, Hq, Hkv, S_max, chunk, nsplit,
+                                 hoff, min(16, G - hoff), flags, scale, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_merge_chunk_kernel<D>), dim3((B * Hq + 3) / 4), dim3(256), 0, stream,
                        part, ctx_len, o, lse, cor, flags, B, Hq, S_max, chunk, nsplit);

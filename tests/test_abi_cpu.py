@@ -98,8 +98,7 @@ def _dec(**kw):
     (dict(ctx=None), binding.PLX_ERR_INVALID_ARG),
     (dict(S=0), binding.PLX_ERR_INVALID_ARG),
     (dict(ns=-1), binding.PLX_ERR_INVALID_ARG),
-    (dict(Hq=6, Hkv=2), binding.PLX_ERR_UNSUPPORTED),  # group of 3
-    (dict(Hq=5, Hkv=2), binding.PLX_ERR_INVALID_ARG),
+    (dict(Hq=5, Hkv=2), binding.PLX_ERR_INVALID_ARG),  # Hq not a multiple of Hkv
     (dict(d=32), binding.PLX_ERR_UNSUPPORTED),
     (dict(d=256, dtype=binding.PLX_F32), binding.PLX_ERR_UNSUPPORTED),
     (dict(ws=None), binding.PLX_ERR_WORKSPACE),
@@ -217,7 +216,7 @@ def _dec_ex(**kw):
     (dict(flags=8), binding.PLX_ERR_INVALID_ARG),
     (dict(cor=ctypes.c_void_p(0x10003)), binding.PLX_ERR_INVALID_ARG),
     (dict(ctx=ctypes.c_void_p(0x10002)), binding.PLX_ERR_INVALID_ARG),
-    (dict(Hq=6, Hkv=2, flags=1), binding.PLX_ERR_UNSUPPORTED),
+    (dict(d=96, flags=2), binding.PLX_ERR_UNSUPPORTED),
     (dict(ws_bytes=16, flags=3), binding.PLX_ERR_WORKSPACE),
 ])
 def test_decode_ex_validation(kw, status):
@@ -321,7 +320,7 @@ def test_decode_noalloc_refuses_problems_beyond_its_buffer():
     big = (64, 16, 1, 1 << 16, 128, 256)
     assert binding.decode_workspace_size(*big) > binding.DECODE_SCRATCH_BYTES
     assert L.plx_decode_noalloc(*args(*big)) == binding.PLX_ERR_WORKSPACE
-    assert L.plx_decode_noalloc(*args(2, 6, 2, 64, 128, 0)) == binding.PLX_ERR_UNSUPPORTED  # G = 3
+    assert L.plx_decode_noalloc(*args(2, 4, 2, 64, 96, 0)) == binding.PLX_ERR_UNSUPPORTED  # d = 96
     assert L.plx_decode_noalloc(*args(2, 4, 2, 0, 128, 0)) == binding.PLX_ERR_INVALID_ARG
     a = list(args(2, 4, 2, 64, 128, 0))
     a[0] = None

@@ -79,6 +79,7 @@ def test_fp32_gradients(gpu_lib, B, Hq, Hkv, T, d):
     (1, 1, 1, 1, 128),     # a single row
     (1, 8, 2, 513, 64),    # G = 4; several 128-key blocks and 64-row query tiles, ragged tail
     (1, 16, 1, 200, 128),  # G = 16: one KV head shared by sixteen query heads
+    (1, 6, 2, 150, 64),    # G = 3
 ])
 def test_bf16_gradients(gpu_lib, B, Hq, Hkv, T, d):
     """Training-workload probe scale, rho ~ N(0, 0.1^2): the bf16 bars."""

@@ -59,6 +59,38 @@ def test_fp32_group_sizes(gpu_lib, G, d):
     check_fp32(got["lse"].reshape(-1), ref["lse"], "lse")
 
 
+@pytest.mark.parametrize("dtype,G,num_splits", [
+    ("bf16", 3, 0), ("bf16", 5, 2), ("bf16", 7, 0), ("bf16", 12, 0), ("bf16", 24, 0), ("bf16", 32, 3),
+    ("f32", 3, 2), ("f32", 24, 2),
+])
+def test_group_sizes_of_any_count(gpu_lib, dtype, G, num_splits):
+    """Any Hq / Hkv, not only powers of two: a group of more than 16 query
+    heads is covered 16 heads at a time, the remainder by the kernel whose
+    column capacity holds it.  Every head matches the oracle, and nothing is
+    written past the workspace (a guard region after it keeps its fill)."""
+    import torch
+
+    from parallax_local_linear_plx_amd import decode_workspace_size, plx_decode
+
+    B, Hkv, S = 2, 2, 300
+    d = 64 if dtype == "f32" else 128
+    say(f"case decode {dtype} G{G} Hq{G * Hkv} Hkv{Hkv} d{d} splits={num_splits}")
+    wl = inputs.make_decode(B, G * Hkv, Hkv, d, 0, S_max=S, dtype=dtype, seed=90 + G, ctx_list=[S, 137],
+                            rho_std=0.5)
+    t = _dev(wl)
+    need = decode_workspace_size(B, wl.Hq, Hkv, S, d, num_splits)
+    ws = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
+    o = torch.full((B, wl.Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    out = plx_decode(t["q"], t["rho"], t["k"], t["v"], t["ctx"], wl.scale, num_splits=num_splits,
+                     workspace=ws, o=o)
+    torch.cuda.synchronize()
+    ref = _oracle(wl)
+    check = check_bf16 if dtype == "bf16" else check_fp32
+    check(out["o"].cpu().numpy().reshape(-1, d), ref["o"], "o")
+    assert np.max(np.abs(out["lse"].cpu().numpy().reshape(-1) - ref["lse"])) <= LSE_ABS
+    assert bool((ws[need:] == 0x5A).all()), "write past the workspace"
+
+
 @pytest.mark.parametrize("num_splits", [0, 1, 5, 64])
 def test_key_count_probe_is_exact(gpu_lib, num_splits):
     """q = 0: exp(LSE) must round to ctx_len[b] exactly for every split count."""

@@ -55,6 +55,7 @@ def test_fp32_gqa_ragged(gpu_lib, B, Hq, Hkv, T, d):
     (1, 2, 2, 129, 64, True),
     (2, 2, 1, 64, 128, False),
     (1, 1, 1, 1, 128, True),
+    (1, 6, 2, 150, 128, False),  # three query heads per KV head
 ])
 def test_bf16_against_oracle(gpu_lib, B, Hq, Hkv, T, d, proj):
     say(f"case bf16 B{B} Hq{Hq} Hkv{Hkv} T{T} d{d} projected-rho={proj}")
