@@ -315,11 +315,13 @@ def bench_proj(steps, warmup):
 
 # ------------------------------------------------------- head-dim variants
 def bench_headdim(steps, warmup):
-    """Prefill (B=4, Hq=16, Hkv=8, T=4096) and decode (B=64, Hq=16, Hkv=8,
-    ctx=8192) at d = 64 and d = 256, for comparison with the d = 128 lines."""
+    """Prefill and backward (B=4, Hq=16, Hkv=8, T=4096) and decode (B=64,
+    Hq=16, Hkv=8, ctx=8192) at d = 64 and d = 256, for comparison with the
+    d = 128 lines."""
     import torch
 
-    from parallax_local_linear_plx_amd import decode_workspace_size, inputs, plx_decode, plx_fwd_prefill
+    from parallax_local_linear_plx_amd import (bwd_workspace_size, decode_workspace_size, inputs, plx_bwd,
+                                               plx_decode, plx_fwd_prefill)
 
     out = {}
     for d in (64, 256):
@@ -331,7 +333,16 @@ def bench_headdim(steps, warmup):
         o = torch.empty((B, Hq, T, d), dtype=torch.float32, device="cuda")
         ms = time_steps(lambda: plx_fwd_prefill(q, k, v, rho, o=o, lse=True), steps, warmup)
         flops = 4 * 2 * d * causal_pairs(T) * B * Hq
-        del q, k, v, rho, o
+        # backward of the same shape (dO ~ N(0, 1))
+        d_o = inputs.device_normal((B, Hq, T, d), 1.0, 79)
+        fwd = plx_fwd_prefill(q, k, v, rho, aux=True)
+        ws_b = torch.empty(bwd_workspace_size(B, Hq, Hkv, T, d), dtype=torch.uint8, device="cuda")
+        grads = {"dq": torch.empty_like(fwd["o"]), "drho": torch.empty_like(fwd["o"]),
+                 "dk": torch.empty((B, Hkv, T, d), dtype=torch.float32, device="cuda"),
+                 "dv": torch.empty((B, Hkv, T, d), dtype=torch.float32, device="cuda")}
+        ms_b = time_steps(lambda: plx_bwd(q, k, v, rho, d_o, fwd["o"], fwd["lse"], fwd["c"], fwd["vbar"],
+                                          workspace=ws_b, grads=grads), steps, warmup)
+        del q, k, v, rho, o, d_o, fwd, ws_b, grads
         Bd, S = 64, 8192
         qd = inputs.device_normal((Bd, Hq, d), 1.0, 75)
         rd = inputs.device_normal((Bd, Hq, d), 0.1, 76)
@@ -346,6 +357,8 @@ def bench_headdim(steps, warmup):
         torch.cuda.empty_cache()
         out[f"d{d}"] = {"prefill_us": ms * 1e3, "prefill_tflops": flops / (ms * 1e-3) / 1e12,
                         "prefill_mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                        "bwd_us": ms_b * 1e3, "bwd_tflops": 2 * flops / (ms_b * 1e-3) / 1e12,
+                        "bwd_mfma_frac": 2 * flops / (ms_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                         "decode_us": msd * 1e3, "decode_GB/s": nbytes / (msd * 1e-3) / 1e9,
                         "decode_hbm_frac": nbytes / (msd * 1e-3) / 1e9 / PEAK_HBM_GBS}
     return out
@@ -572,7 +585,7 @@ def main():
         return
     if args.only == "headdim":
         log("head-dim variants ...")
-        print(json.dumps({"metric": "prefill TFLOP/s and decode GB/s at d = 64 and 256", "n_gpus": 1,
+        print(json.dumps({"metric": "prefill and backward TFLOP/s, decode GB/s at d = 64 and 256", "n_gpus": 1,
                           "dtype": "bf16", "data": "synthetic",
                           "headdim": bench_headdim(max(10, args.steps // 2), max(10, args.warmup // 2))}),
               flush=True)
