@@ -43,6 +43,14 @@ template <int D>
 constexpr int f16_bc() { return D > 128 ? 64 : F16_BC; }
 template <int D>
 constexpr int f16_waves() { return D > 128 ? 4 : FWD16_WAVES; }
+// 16-row query blocks per wave: at d = 64 a wave's state leaves room for two,
+// which share every K and V^T operand read from LDS (half the LDS traffic and
+// half the softmax-independent instructions per MFMA).
+#ifndef PLX_RB64
+#define PLX_RB64 2
+#endif
+template <int D>
+constexpr int f16_row_blocks() { return D == 64 ? PLX_RB64 : 1; }
 // Lazy-rescale threshold (log2 units): p stays <= 16, so the fp16 operand
 // p * r overflows only for |r| = |rho . k| > 4094.
 constexpr float kRescaleLog2 = 4.f;
@@ -508,7 +516,9 @@ __global__ __launch_bounds__(FWD_THREADS, 1) void fwd_kernel(
 // double-buffered in LDS (K bf16 rows, V fp16 rows); the global loads of tile
 // j+1 are issued at the start of tile j and stored at its end, before the
 // tile's single barrier.  At d = 256 the workgroup is 4 waves (64 rows, one
-// wave per SIMD) and the tiles 64 keys (f16_bc, f16_waves).
+// wave per SIMD) and the tiles 64 keys (f16_bc, f16_waves).  At d = 64 a wave
+// takes two 16-row blocks (RB = 2, 256 rows per workgroup): each K and V^T
+// operand read from LDS feeds both blocks' MFMAs (f16_row_blocks).
 template <int D>
 struct Fwd16Smem {
   // row strides (elements), chosen so that the ds_read_b128 of K and the
@@ -527,14 +537,14 @@ struct Fwd16Smem {
 // p r (|r| up to tens) shifts c by ~1e-2 on rows with few keys, and the
 // backward's dV = sum_i w_ij (1 + c_i - r_ij) dO_i carries that shift
 // straight through.
-template <int D, int NW, bool AUX>
+template <int D, int NW, int RB, bool AUX>
 __global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ rho, float* __restrict__ o, float* __restrict__ lse,
     float* __restrict__ c_aux, float* __restrict__ vbar_aux, float* __restrict__ cor,
     unsigned flags, int B, int Hq, int Hkv, int T, float scale_log2) {
   constexpr int NT = 64 * NW;       // threads
-  constexpr int BR = 16 * NW;       // query rows per workgroup
+  constexpr int BR = 16 * NW * RB;  // query rows per workgroup
   constexpr int NS = D / 32;        // score MFMA steps over d
   constexpr int ND = D / 16;        // 16-row d tiles of O^T / U^T
   constexpr int CPR = D / 8;        // 16-byte chunks per row
@@ -555,8 +565,8 @@ __global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int q0 = qb * BR;
-  const int qw = q0 + 16 * wave;  // first query of this wave
-  const int my_q = qw + c;
+  // the wave's RB blocks of 16 rows: block rb starts at qw + 16 rb
+  const int qw = q0 + 16 * RB * wave;
 
   const uint16_t* qp = q + ((size_t)bh * T) * D;
   const uint16_t* rp = rho + ((size_t)bh * T) * D;
@@ -565,8 +575,8 @@ __global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
 
   const int kend = min(T, q0 + BR);
   const int ntiles = (kend + BC - 1) / BC;
-  // 32-key sub-tiles this wave attends to: keys [0, min(kend, qw + 16))
-  const int nsub = (min(kend, qw + 16) + 31) / 32;
+  // 32-key sub-tiles this wave attends to: keys [0, min(kend, last row + 1))
+  const int nsub = (min(kend, qw + 16 * RB) + 31) / 32;
 
   // global -> register prefetch of one K / V tile (rows past T read row T-1:
   // finite, and masked by the causal test since they follow every query)
@@ -613,41 +623,57 @@ __global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
   // Uniform weights: a zero query operand makes every score exactly 0, so
   // every unmasked key gets p = 1 and the running max stays 0.
   const bool use_q = !(flags & PLX_UNIFORM_WEIGHTS);
-  bf16x8 qop[NS], rop[NS];
+  bf16x8 qop[RB][NS], rop[RB][NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4 qa = {0u, 0u, 0u, 0u}, ra = {0u, 0u, 0u, 0u};
-    if (my_q < T) {
-      if (use_q) qa = *reinterpret_cast<const u32x4*>(qp + (size_t)my_q * D + 32 * s + 8 * g);
-      ra = *reinterpret_cast<const u32x4*>(rp + (size_t)my_q * D + 32 * s + 8 * g);
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int my_q = qw + 16 * rb + c;
+      u32x4 qa = {0u, 0u, 0u, 0u}, ra = {0u, 0u, 0u, 0u};
+      if (my_q < T) {
+        if (use_q) qa = *reinterpret_cast<const u32x4*>(qp + (size_t)my_q * D + 32 * s + 8 * g);
+        ra = *reinterpret_cast<const u32x4*>(rp + (size_t)my_q * D + 32 * s + 8 * g);
+      }
+      qop[rb][s] = __builtin_bit_cast(bf16x8, qa);
+      rop[rb][s] = __builtin_bit_cast(bf16x8, ra);
     }
-    qop[s] = __builtin_bit_cast(bf16x8, qa);
-    rop[s] = __builtin_bit_cast(bf16x8, ra);
-  }
   lds_put(preA, 0);
   __syncthreads();
 
-  f32x4 oacc[ND], uacc[ND];
+  f32x4 oacc[RB][ND], uacc[RB][ND];
 #pragma unroll
-  for (int i = 0; i < ND; ++i) {
-    oacc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    uacc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  }
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      oacc[rb][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      uacc[rb][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
   // l and C as MFMAs against an all-ones A operand: every row of lacc / cacc
   // holds the column (query) sum over the keys of the rounded P / P.R
-  f32x4 lacc = {0.f, 0.f, 0.f, 0.f}, cacc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 lacc[RB], cacc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    lacc[rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    cacc[rb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
   f16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (_Float16)1.f;
   asm volatile("" : "+v"(ones));  // kept in registers, not rebuilt per sub-tile
   // e_part: this lane's unrounded sum of p (the LSE only); ce_part: the
   // unrounded sum of p r (c_aux only)
-  float m_run = -INFINITY, e_part = 0.f, ce_part = 0.f;
+  float m_run[RB], e_part[RB], ce_part[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = -INFINITY;
+    e_part[rb] = 0.f;
+    ce_part[rb] = 0.f;
+  }
 
   auto subtile = [&](int kbuf, int vbuf, int st, int kbase) {
     // scores
     __builtin_amdgcn_s_setprio(1);
-    f32x4 sacc[2], racc[2];
+    f32x4 sacc[RB][2], racc[RB][2];
     unsigned kaddr = lds_addr(&sm.k[kbuf][(32 * st + c) * SM::KLD + 8 * g]);
     asm volatile("" : "+v"(kaddr));
     // every K operand of the sub-tile in flight before the first MFMA
@@ -663,10 +689,13 @@ __global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const bf16x8 a = ka[t][s];
-        const f32x4 zs = s == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : sacc[t];
-        const f32x4 zr = s == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : racc[t];
-        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[s], zs, 0, 0, 0);
-        racc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rop[s], zr, 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const f32x4 zs = s == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : sacc[rb][t];
+          const f32x4 zr = s == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : racc[rb][t];
+          sacc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[rb][s], zs, 0, 0, 0);
+          racc[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, rop[rb][s], zr, 0, 0, 0);
+        }
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -680,71 +709,79 @@ __global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
       va[dt][1] = tr16_at(vaddr + 2 * (16 * dt + 16 * SM::VLD));
     }
     __builtin_amdgcn_sched_barrier(0);
-    // causal mask where the sub-tile reaches past the wave's first query
-    if (kbase + 31 > qw) {
+    f16x8 pop[RB], prop[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int qr = qw + 16 * rb;  // first query of this row block
+      const int my_q = qr + c;
+      // causal mask where the sub-tile reaches past the block's first query
+      if (kbase + 31 > qr) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (kbase + 16 * t + 4 * g + j > my_q) sacc[rb][t][j] = -INFINITY;
+      }
+      float mt = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (kbase + 16 * t + 4 * g + j > my_q) sacc[t][j] = -INFINITY;
-    }
-    float mt = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mt = fmaxf(mt, sacc[t][j]);
-    {
-      // max over the four 16-lane groups: permlane swaps, no LDS round trip
-      // (NaN-propagating maximum: no canonicalising moves around the swaps)
-      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-      mt = __builtin_elementwise_maximum(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-      mt = __builtin_elementwise_maximum(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
-    }
-    mt *= scale_log2;
-    // lazy rescale: the reference max moves only when a row's max exceeds it
-    // by more than kRescaleLog2, so p <= 2^kRescaleLog2 in between
-    if (__any(mt > m_run + kRescaleLog2)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float m_u = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_u);
-      e_part *= alpha;
-      if constexpr (AUX) ce_part *= alpha;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        lacc[jj] *= alpha;
-        cacc[jj] *= alpha;
+        for (int j = 0; j < 4; ++j) mt = fmaxf(mt, sacc[rb][t][j]);
+      {
+        // max over the four 16-lane groups: permlane swaps, no LDS round trip
+        // (NaN-propagating maximum: no canonicalising moves around the swaps)
+        const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = __builtin_elementwise_maximum(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = __builtin_elementwise_maximum(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
       }
+      mt *= scale_log2;
+      // lazy rescale: the reference max moves only when a row's max exceeds it
+      // by more than kRescaleLog2, so p <= 2^kRescaleLog2 in between
+      if (__any(mt > m_run[rb] + kRescaleLog2)) {
+        const float m_new = fmaxf(m_run[rb], mt);
+        const float m_u = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run[rb] - m_u);
+        e_part[rb] *= alpha;
+        if constexpr (AUX) ce_part[rb] *= alpha;
 #pragma unroll
-      for (int i = 0; i < ND; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          oacc[i][j] *= alpha;
-          uacc[i][j] *= alpha;
+        for (int jj = 0; jj < 4; ++jj) {
+          lacc[rb][jj] *= alpha;
+          cacc[rb][jj] *= alpha;
         }
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    f16x8 pop, prop;
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const float s0 = sacc[e >> 2][e & 3], s1 = sacc[e >> 2][(e & 3) + 1];
-      const float p0 = fast_exp2(__builtin_fmaf(s0, scale_log2, -m_use));
-      const float p1 = fast_exp2(__builtin_fmaf(s1, scale_log2, -m_use));
-      e_part += p0 + p1;
-      const float pr0 = p0 * racc[e >> 2][e & 3], pr1 = p1 * racc[e >> 2][(e & 3) + 1];
-      if constexpr (AUX) ce_part += pr0 + pr1;
-      const f16x2 ph = {(_Float16)p0, (_Float16)p1};
-      const f16x2 rh = {(_Float16)pr0, (_Float16)pr1};
-      pop[e] = ph[0];
-      pop[e + 1] = ph[1];
-      prop[e] = rh[0];
-      prop[e + 1] = rh[1];
+        for (int i = 0; i < ND; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            oacc[rb][i][j] *= alpha;
+            uacc[rb][i][j] *= alpha;
+          }
+        m_run[rb] = m_new;
+      }
+      const float m_use = (m_run[rb] == -INFINITY) ? 0.f : m_run[rb];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float s0 = sacc[rb][e >> 2][e & 3], s1 = sacc[rb][e >> 2][(e & 3) + 1];
+        const float p0 = fast_exp2(__builtin_fmaf(s0, scale_log2, -m_use));
+        const float p1 = fast_exp2(__builtin_fmaf(s1, scale_log2, -m_use));
+        e_part[rb] += p0 + p1;
+        const float pr0 = p0 * racc[rb][e >> 2][e & 3], pr1 = p1 * racc[rb][e >> 2][(e & 3) + 1];
+        if constexpr (AUX) ce_part[rb] += pr0 + pr1;
+        const f16x2 ph = {(_Float16)p0, (_Float16)p1};
+        const f16x2 rh = {(_Float16)pr0, (_Float16)pr1};
+        pop[rb][e] = ph[0];
+        pop[rb][e + 1] = ph[1];
+        prop[rb][e] = rh[0];
+        prop[rb][e + 1] = rh[1];
+      }
     }
     __builtin_amdgcn_s_setprio(1);
-    lacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop, lacc, 0, 0, 0);
-    cacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, prop, cacc, 0, 0, 0);
-    // value MFMAs
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      lacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pop[rb], lacc[rb], 0, 0, 0);
+      cacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, prop[rb], cacc[rb], 0, 0, 0);
+    }
+    // value MFMAs: every V^T operand feeds the RB row blocks
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
       const f16x4 v0 = va[dt][0], v1 = va[dt][1];
@@ -754,8 +791,11 @@ __global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
         av[e] = v0[e];
         av[4 + e] = v1[e];
       }
-      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pop, oacc[dt], 0, 0, 0);
-      uacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, prop, uacc[dt], 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        oacc[rb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pop[rb], oacc[rb][dt], 0, 0, 0);
+        uacc[rb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, prop[rb], uacc[rb][dt], 0, 0, 0);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -777,54 +817,58 @@ __global__ __launch_bounds__(64 * NW, (D > 128) ? 1 : 8 / NW) void fwd16_kernel(
     if (j + 1 < ntiles) iter(j + 1, 1);
   }
 
-  // epilogue: o = (O/l)(1 + C/l) - U/l (without an intercept: -U/l);
-  // LSE = ln sum exp(scaled scores); COR = ||U/l - (O/l)(C/l)|| / ||o||
+  // epilogue, per row block: o = (O/l)(1 + C/l) - U/l (without an intercept:
+  // -U/l); LSE = ln sum exp(scaled scores); COR = ||U/l - (O/l)(C/l)|| / ||o||
   // (without an intercept the correction is U/l).  The lanes of one query
   // (same c, g = 0..3) hold disjoint quarters of its d values.
-  const float l_tot = lacc[0], c_tot = cacc[0];
-  float e_tot = e_part;
-  e_tot += __shfl_xor(e_tot, 16, 64);
-  e_tot += __shfl_xor(e_tot, 32, 64);
-  float ce_tot = ce_part;
-  if constexpr (AUX) {
-    ce_tot += __shfl_xor(ce_tot, 16, 64);
-    ce_tot += __shfl_xor(ce_tot, 32, 64);
-  }
-  const float inv = 1.f / l_tot;
-  const float cc = c_tot * inv;
   const bool no_icpt = flags & PLX_NO_INTERCEPT;
-  f32x4 ov[ND], vv[ND];
-  float n_o = 0.f, n_c = 0.f;
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const float vbar = oacc[dt][jj] * inv;
-      const float u = uacc[dt][jj] * inv;
-      vv[dt][jj] = vbar;
-      ov[dt][jj] = no_icpt ? -u : vbar * (1.f + cc) - u;
-      const float corr = no_icpt ? u : u - vbar * cc;
-      n_o = __builtin_fmaf(ov[dt][jj], ov[dt][jj], n_o);
-      n_c = __builtin_fmaf(corr, corr, n_c);
+  for (int rb = 0; rb < RB; ++rb) {
+    const int my_q = qw + 16 * rb + c;
+    const float l_tot = lacc[rb][0], c_tot = cacc[rb][0];
+    float e_tot = e_part[rb];
+    e_tot += __shfl_xor(e_tot, 16, 64);
+    e_tot += __shfl_xor(e_tot, 32, 64);
+    float ce_tot = ce_part[rb];
+    if constexpr (AUX) {
+      ce_tot += __shfl_xor(ce_tot, 16, 64);
+      ce_tot += __shfl_xor(ce_tot, 32, 64);
     }
-  if (cor) {
-    n_o += __shfl_xor(n_o, 16, 64);
-    n_o += __shfl_xor(n_o, 32, 64);
-    n_c += __shfl_xor(n_c, 16, 64);
-    n_c += __shfl_xor(n_c, 32, 64);
-  }
-  if (my_q < T) {
-    float* orow = o + ((size_t)bh * T + my_q) * D;
-    float* vrow = vbar_aux ? vbar_aux + ((size_t)bh * T + my_q) * D : nullptr;
+    const float inv = 1.f / l_tot;
+    const float cc = c_tot * inv;
+    f32x4 ov[ND], vv[ND];
+    float n_o = 0.f, n_c = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * g) = ov[dt];
-      if (vrow) *reinterpret_cast<f32x4*>(vrow + 16 * dt + 4 * g) = vv[dt];
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float vbar = oacc[rb][dt][jj] * inv;
+        const float u = uacc[rb][dt][jj] * inv;
+        vv[dt][jj] = vbar;
+        ov[dt][jj] = no_icpt ? -u : vbar * (1.f + cc) - u;
+        const float corr = no_icpt ? u : u - vbar * cc;
+        n_o = __builtin_fmaf(ov[dt][jj], ov[dt][jj], n_o);
+        n_c = __builtin_fmaf(corr, corr, n_c);
+      }
+    if (cor) {
+      n_o += __shfl_xor(n_o, 16, 64);
+      n_o += __shfl_xor(n_o, 32, 64);
+      n_c += __shfl_xor(n_c, 16, 64);
+      n_c += __shfl_xor(n_c, 32, 64);
     }
-    if (g == 0) {
-      if (lse) lse[(size_t)bh * T + my_q] = (m_run + __log2f(e_tot)) * kLn2;
-      if constexpr (AUX) c_aux[(size_t)bh * T + my_q] = ce_tot / e_tot;
-      if (cor) cor[(size_t)bh * T + my_q] = __builtin_sqrtf(n_c) / __builtin_sqrtf(n_o);
+    if (my_q < T) {
+      float* orow = o + ((size_t)bh * T + my_q) * D;
+      float* vrow = vbar_aux ? vbar_aux + ((size_t)bh * T + my_q) * D : nullptr;
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * g) = ov[dt];
+        if (vrow) *reinterpret_cast<f32x4*>(vrow + 16 * dt + 4 * g) = vv[dt];
+      }
+      if (g == 0) {
+        if (lse) lse[(size_t)bh * T + my_q] = (m_run[rb] + __log2f(e_tot)) * kLn2;
+        if constexpr (AUX) c_aux[(size_t)bh * T + my_q] = ce_tot / e_tot;
+        if (cor) cor[(size_t)bh * T + my_q] = __builtin_sqrtf(n_c) / __builtin_sqrtf(n_o);
+      }
     }
   }
 }
@@ -833,13 +877,14 @@ template <int D, int NW>
 hipError_t launch_fwd16(const void* q, const void* k, const void* v, const void* rho, float* o,
                         float* lse, float* c_aux, float* vbar_aux, float* cor, unsigned flags, int B,
                         int Hq, int Hkv, int T, float scale, hipStream_t stream) {
-  const int nqb = (T + 16 * NW - 1) / (16 * NW);
+  constexpr int RB = f16_row_blocks<D>();
+  const int nqb = (T + 16 * NW * RB - 1) / (16 * NW * RB);
   if (c_aux)
-    hipLaunchKernelGGL((fwd16_kernel<D, NW, true>), dim3(nqb * B * Hq), dim3(64 * NW), 0, stream,
+    hipLaunchKernelGGL((fwd16_kernel<D, NW, RB, true>), dim3(nqb * B * Hq), dim3(64 * NW), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)rho,
                        o, lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale * kLog2e);
   else
-    hipLaunchKernelGGL((fwd16_kernel<D, NW, false>), dim3(nqb * B * Hq), dim3(64 * NW), 0, stream,
+    hipLaunchKernelGGL((fwd16_kernel<D, NW, RB, false>), dim3(nqb * B * Hq), dim3(64 * NW), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)rho,
                        o, lse, c_aux, vbar_aux, cor, flags, B, Hq, Hkv, T, scale * kLog2e);
   return hipGetLastError();
