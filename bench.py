@@ -646,7 +646,7 @@ def main():
                                   "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                   "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4),
                                   "traffic": measured_traffic("prefill"),
-                                  "kernel": "fwd16_kernel<128,8>",
+                                  "kernel": "fwd16_kernel<128,8,1,false>",
                                   **({"measured_peak": peaks["mfma_bf16_tflops"],
                                       "frac_of_measured": round(p["tflops"] / peaks["mfma_bf16_tflops"], 4)}
                                      if peaks else {}),
