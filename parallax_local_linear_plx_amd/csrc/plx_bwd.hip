@@ -21,9 +21,10 @@
 //   dkdv  : key-outer: one key per lane column (S = Q K^T), loops over the
 //           query tiles of every head that shares the KV head, accumulates
 //           dV^T = dO^T Ptilde and dK^T = Q^T (tau dS) + rho^T dR.
-// The bf16 dq and dkdv kernels run 16-row waves on 16x16x32 fp16 MFMAs, two
-// waves per SIMD; the fp32 ones (the exact-parity path) 32-row waves on fp32
-// MFMAs.
+// The bf16 dq and dkdv kernels run 16-row blocks on 16x16x32 fp16 MFMAs, two
+// waves per SIMD; at d = 64 each wave carries two blocks (query rows in dq,
+// keys in dkdv) so that one LDS operand read feeds both.  The fp32 kernels
+// (the exact-parity path) run 32-row waves on fp32 MFMAs.
 #include <algorithm>
 #include <type_traits>
 
@@ -416,6 +417,12 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv_kernel(
 // exact, so the result does not depend on the scale of dO except through
 // fp32 underflow or overflow of the gradients themselves.
 inline size_t bwd_ws_align(size_t n) { return (n + 255) & ~(size_t)255; }
+#ifndef PLX_KB64
+#define PLX_KB64 2
+#endif
+#ifndef PLX_QB64
+#define PLX_QB64 2
+#endif
 
 // Workgroups of the preparation pass: each reduces its part of dO to one
 // partial maximum, which bounds the partials buffer in the workspace.
@@ -508,7 +515,9 @@ struct DqbSmem {
   alignas(16) uint16_t v[2][BC * LD];  // bf16, as stored
 };
 
-template <int D, int NW, int BC>
+// QB: 16-row query blocks per wave; each K / V operand read from LDS feeds
+// the MFMAs of all QB blocks (QB = 2 at d = 64, where the registers allow it).
+template <int D, int NW, int BC, int QB>
 __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k16, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ rho, const uint16_t* __restrict__ d_o, const float* __restrict__ o,
@@ -517,7 +526,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
     _Float16* __restrict__ r16, _Float16* __restrict__ g16, const float* __restrict__ dsc,
     float* __restrict__ dq, float* __restrict__ drho, int B, int Hq, int Hkv, int T, float scale,
     float scale_log2) {
-  constexpr int NT = 64 * NW, BR = 16 * NW;
+  constexpr int NT = 64 * NW, BR = 16 * NW * QB;
   constexpr int NS = D / 32, ND = D / 16, CPR = D / 8;
   constexpr int NCH = BC * CPR / NT;  // 16-byte chunks per thread per tile and tensor
   using SM = DqbSmem<D, BC>;
@@ -534,16 +543,14 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int q0 = qb * BR;
-  const int qw = q0 + 16 * wave;
-  const int my_q = qw + c;
-  const bool qvalid = my_q < T;
+  const int qw = q0 + 16 * QB * wave;  // first query of the wave; block qb2 starts at qw + 16 qb2
 
   const size_t rowbase = (size_t)bh * T;
   const uint16_t* kp = k16 + ((size_t)(b * Hkv + hk) * T) * D;
   const uint16_t* vp = v + ((size_t)(b * Hkv + hk) * T) * D;
   const int kend = min(T, q0 + BR);
   const int ntiles = (kend + BC - 1) / BC;
-  const int nsub = (min(kend, qw + 16) + 31) / 32;
+  const int nsub = (min(kend, qw + 16 * QB) + 31) / 32;
 
   // global -> register staging of one tile (rows past T read row T-1: finite,
   // and masked by the causal test since they follow every query)
@@ -582,10 +589,17 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
   gload(0);
   // dO scale s and 1 / s (powers of two, from the preparation pass)
   const float gsc = dsc[0], ginv = dsc[1];
-  // this lane's quarter of its query row: elements 32 s + 8 g .. + 8
-  f16x8 qop[NS], rop[NS];
-  bf16x8 gop[NS];
-  float Gi = 0.f, di = 0.f;
+  // this lane's quarter of its query rows: elements 32 s + 8 g .. + 8
+  f16x8 qop[QB][NS], rop[QB][NS];
+  bf16x8 gop[QB][NS];
+  // per query row: lse * log2e, delta, and (dS = p [A k1 + r (delta - A) - k2])
+  // k1 = 1 + c, k2 = G + delta c
+  float lse2[QB], di[QB], k1[QB], k2[QB];
+#pragma unroll
+  for (int qb2 = 0; qb2 < QB; ++qb2) {
+  const int my_q = qw + 16 * qb2 + c;
+  const bool qvalid = my_q < T;
+  float Gi = 0.f, dd = 0.f;
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     u32x4 qa = {0u, 0u, 0u, 0u}, ra = qa, ga = qa;
@@ -610,41 +624,45 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
       for (int e = 0; e < 4; ++e) {
         const float x0 = bf16_bits_to_f32(gb[e]), x1 = bf16_bits_to_f32(gb[4 + e]);
         Gi = __builtin_fmaf(x0, o0[e], __builtin_fmaf(x1, o1[e], Gi));
-        di = __builtin_fmaf(x0, v0[e], __builtin_fmaf(x1, v1[e], di));
+        dd = __builtin_fmaf(x0, v0[e], __builtin_fmaf(x1, v1[e], dd));
       }
     }
-    qop[s] = cvt_bf16x8_f16(qa);
-    rop[s] = cvt_bf16x8_f16(ra);
-    gop[s] = __builtin_bit_cast(bf16x8, ga);
+    qop[qb2][s] = cvt_bf16x8_f16(qa);
+    rop[qb2][s] = cvt_bf16x8_f16(ra);
+    gop[qb2][s] = __builtin_bit_cast(bf16x8, ga);
     if (qvalid) {
       const size_t off = (rowbase + my_q) * D + 32 * s + 8 * g;
-      *reinterpret_cast<f16x8*>(q16 + off) = qop[s];
-      *reinterpret_cast<f16x8*>(r16 + off) = rop[s];
+      *reinterpret_cast<f16x8*>(q16 + off) = qop[qb2][s];
+      *reinterpret_cast<f16x8*>(r16 + off) = rop[qb2][s];
       *reinterpret_cast<f16x8*>(g16 + off) = cvt_bf16x8_f16(ga);
     }
   }
   // the four 16-lane groups hold disjoint quarters of the row
   Gi += __shfl_xor(Gi, 16, 64);
   Gi += __shfl_xor(Gi, 32, 64);
-  di += __shfl_xor(di, 16, 64);
-  di += __shfl_xor(di, 32, 64);
+  dd += __shfl_xor(dd, 16, 64);
+  dd += __shfl_xor(dd, 32, 64);
   if (qvalid && g == 0) {
     Gv[rowbase + my_q] = Gi;
-    dlt[rowbase + my_q] = di;
+    dlt[rowbase + my_q] = dd;
   }
-  const float lse2 = qvalid ? lse[rowbase + my_q] * kLog2e : 0.f;
+  lse2[qb2] = qvalid ? lse[rowbase + my_q] * kLog2e : 0.f;
   const float ci = qvalid ? c_aux[rowbase + my_q] : 0.f;
-  // dS = p [A k1 + r (delta - A) - k2] with k1 = 1 + c, k2 = G + delta c
-  const float k1 = 1.f + ci, k2 = Gi + di * ci;
+  di[qb2] = dd;
+  k1[qb2] = 1.f + ci;
+  k2[qb2] = Gi + dd * ci;
+  }  // query blocks
   lds_put(0);
   __syncthreads();
 
-  f32x4 dqa[ND], dra[ND];
+  f32x4 dqa[QB][ND], dra[QB][ND];
 #pragma unroll
-  for (int i = 0; i < ND; ++i) {
-    dqa[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    dra[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  }
+  for (int qb2 = 0; qb2 < QB; ++qb2)
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      dqa[qb2][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      dra[qb2][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
 
   auto subtile = [&](int buf, int st, int kbase) {
     // scores S^T, R^T and A^T = V dO^T for 32 keys
@@ -662,16 +680,18 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
       }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
-    f32x4 sacc[2], racc[2], aacc[2];
+    f32x4 sacc[QB][2], racc[QB][2], aacc[QB][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[t][s], qop[s], s == 0 ? z : sacc[t], 0, 0, 0);
-        racc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[t][s], rop[s], s == 0 ? z : racc[t], 0, 0, 0);
-        aacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[t][s], gop[s], s == 0 ? z : aacc[t], 0, 0, 0);
-      }
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int qb2 = 0; qb2 < QB; ++qb2) {
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          sacc[qb2][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[t][s], qop[qb2][s], s == 0 ? z : sacc[qb2][t], 0, 0, 0);
+          racc[qb2][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[t][s], rop[qb2][s], s == 0 ? z : racc[qb2][t], 0, 0, 0);
+          aacc[qb2][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[t][s], gop[qb2][s], s == 0 ? z : aacc[qb2][t], 0, 0, 0);
+        }
     }
     __builtin_amdgcn_s_setprio(0);
     // K^T operands of the gradient MFMAs, in flight during the elementwise part
@@ -688,28 +708,34 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
     // stay in place instead of being copied where two variants would join)
     if (kbase + 31 > qw) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int qb2 = 0; qb2 < QB; ++qb2)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (kbase + 16 * t + 4 * g + j > my_q) sacc[t][j] = -INFINITY;
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (kbase + 16 * t + 4 * g + j > qw + 16 * qb2 + c) sacc[qb2][t][j] = -INFINITY;
     }
     // dS^T, dR^T: element e of group g is key 16 (e / 4) + 4 g + e % 4, query c
-    f16x8 dsop, drop;
+    f16x8 dsop[QB], drop[QB];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = e >> 2, j = e & 3;
-      const float p = fast_exp2(__builtin_fmaf(sacc[t][j], scale_log2, -lse2));
-      const float r = racc[t][j], A = aacc[t][j];
-      const float tt = di - A;
-      dsop[e] = (_Float16)(p * __builtin_fmaf(A, k1, __builtin_fmaf(r, tt, -k2)));
-      drop[e] = (_Float16)(p * tt);
-    }
+    for (int qb2 = 0; qb2 < QB; ++qb2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int t = e >> 2, j = e & 3;
+        const float p = fast_exp2(__builtin_fmaf(sacc[qb2][t][j], scale_log2, -lse2[qb2]));
+        const float r = racc[qb2][t][j], A = aacc[qb2][t][j];
+        const float tt = di[qb2] - A;
+        dsop[qb2][e] = (_Float16)(p * __builtin_fmaf(A, k1[qb2], __builtin_fmaf(r, tt, -k2[qb2])));
+        drop[qb2][e] = (_Float16)(p * tt);
+      }
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      dqa[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kt[dt], dsop, dqa[dt], 0, 0, 0);
-      dra[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kt[dt], drop, dra[dt], 0, 0, 0);
-    }
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int qb2 = 0; qb2 < QB; ++qb2) {
+        dqa[qb2][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kt[dt], dsop[qb2], dqa[qb2][dt], 0, 0, 0);
+        dra[qb2][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kt[dt], drop[qb2], dra[qb2][dt], 0, 0, 0);
+      }
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -729,20 +755,24 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
     if (j + 1 < ntiles) iter(j + 1, 1);
   }
 
-  // dqa[dt][jj] is d = 16 dt + 4 g + jj of query c
-  if (qvalid) {
-    float* dqr = dq + (rowbase + my_q) * D;
-    float* drr = drho + (rowbase + my_q) * D;
+  // dqa[qb2][dt][jj] is d = 16 dt + 4 g + jj of query qw + 16 qb2 + c
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      f32x4 x, y;
+  for (int qb2 = 0; qb2 < QB; ++qb2) {
+    const int my_q = qw + 16 * qb2 + c;
+    if (my_q < T) {
+      float* dqr = dq + (rowbase + my_q) * D;
+      float* drr = drho + (rowbase + my_q) * D;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        x[jj] = (scale * ginv) * dqa[dt][jj];
-        y[jj] = ginv * dra[dt][jj];
+      for (int dt = 0; dt < ND; ++dt) {
+        f32x4 x, y;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          x[jj] = (scale * ginv) * dqa[qb2][dt][jj];
+          y[jj] = ginv * dra[qb2][dt][jj];
+        }
+        *reinterpret_cast<f32x4*>(dqr + 16 * dt + 4 * g) = x;
+        *reinterpret_cast<f32x4*>(drr + 16 * dt + 4 * g) = y;
       }
-      *reinterpret_cast<f32x4*>(dqr + 16 * dt + 4 * g) = x;
-      *reinterpret_cast<f32x4*>(drr + 16 * dt + 4 * g) = y;
     }
   }
 }
@@ -767,14 +797,16 @@ struct DkbSmem {
   alignas(16) float sc[2][BQ][4];  // per query row: lse * log2e, 1 + c, G + delta c, delta
 };
 
-template <int D, int NW, int BQ>
+// KB: 16-key blocks per wave; each query-tile operand read from LDS feeds
+// the MFMAs of all KB blocks (KB = 2 at d = 64, where the registers allow it).
+template <int D, int NW, int BQ, int KB>
 __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ rho, const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
     const float* __restrict__ c_aux, const float* __restrict__ Gv, const float* __restrict__ dlt,
     const float* __restrict__ dsc, float* __restrict__ dk, float* __restrict__ dv, int B, int Hq,
     int Hkv, int T, float scale, float scale_log2) {
-  constexpr int NT = 64 * NW, BK = 16 * NW;
+  constexpr int NT = 64 * NW, BK = 16 * NW * KB;
   constexpr int NS = D / 32, ND = D / 16, CPR = D / 8;
   constexpr int NCH = BQ * CPR / NT;  // 16-byte chunks per thread per tile and tensor
   using SM = DkbSmem<D, BQ>;
@@ -789,9 +821,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int k0 = kb * BK;
-  const int kw = k0 + 16 * wave;
-  const int my_k = kw + c;
-  const bool kvalid = my_k < T;
+  const int kw = k0 + 16 * KB * wave;  // first key of the wave; block kb2 starts at kw + 16 kb2
 
   const size_t kvbase = (size_t)bhk * T;
   const float ginv = dsc[1];  // 1 / s of the dO scale
@@ -862,31 +892,36 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
   };
 
   gload(0);
-  f16x8 kop[NS], vop[NS];
+  f16x8 kop[KB][NS], vop[KB][NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4 ka = {0u, 0u, 0u, 0u}, va = ka;
-    if (kvalid) {
-      const size_t off = (kvbase + my_k) * D + 32 * s + 8 * g;
-      ka = *reinterpret_cast<const u32x4*>(k + off);
-      va = *reinterpret_cast<const u32x4*>(v + off);
+  for (int kb2 = 0; kb2 < KB; ++kb2)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int my_k = kw + 16 * kb2 + c;
+      u32x4 ka = {0u, 0u, 0u, 0u}, va = ka;
+      if (my_k < T) {
+        const size_t off = (kvbase + my_k) * D + 32 * s + 8 * g;
+        ka = *reinterpret_cast<const u32x4*>(k + off);
+        va = *reinterpret_cast<const u32x4*>(v + off);
+      }
+      kop[kb2][s] = cvt_bf16x8_f16(ka);  // K and V as stored (bf16), converted once here
+      vop[kb2][s] = cvt_bf16x8_f16(va);
     }
-    kop[s] = cvt_bf16x8_f16(ka);  // K and V as stored (bf16), converted once here
-    vop[s] = cvt_bf16x8_f16(va);
-  }
   lds_put(0);
   __syncthreads();
 
-  f32x4 dka[ND], dva[ND];
+  f32x4 dka[KB][ND], dva[KB][ND];
 #pragma unroll
-  for (int i = 0; i < ND; ++i) {
-    dka[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    dva[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  }
+  for (int kb2 = 0; kb2 < KB; ++kb2)
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      dka[kb2][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      dva[kb2][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
 
   // one 32-query sub-tile st of the tile in buffer buf (first query qs)
   auto subtile = [&](int buf, int st, int qs) {
-    f32x4 sacc[2], racc[2], aacc[2];
+    f32x4 sacc[KB][2], racc[KB][2], aacc[KB][2];
     {
       unsigned qa = lds_addr(&sm.q[buf][(32 * st + c) * SM::LD + 8 * g]);
       unsigned ra = lds_addr(&sm.r[buf][(32 * st + c) * SM::LD + 8 * g]);
@@ -906,12 +941,14 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qo[s], kop[s], s == 0 ? z : sacc[t], 0, 0, 0);
-          racc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ro[s], kop[s], s == 0 ? z : racc[t], 0, 0, 0);
-          aacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(go[s], vop[s], s == 0 ? z : aacc[t], 0, 0, 0);
-        }
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+          for (int kb2 = 0; kb2 < KB; ++kb2) {
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            sacc[kb2][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qo[s], kop[kb2][s], s == 0 ? z : sacc[kb2][t], 0, 0, 0);
+            racc[kb2][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ro[s], kop[kb2][s], s == 0 ? z : racc[kb2][t], 0, 0, 0);
+            aacc[kb2][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(go[s], vop[kb2][s], s == 0 ? z : aacc[kb2][t], 0, 0, 0);
+          }
         __builtin_amdgcn_s_setprio(0);
       }
     }
@@ -919,16 +956,18 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
     // the same order as the K index of the transpose-read A operands below.
     // Causal mask (queries before the key) and rows past T, in a uniform
     // branch: one code path for every sub-tile (see the dQ kernel).
-    if (qs < kw + 15 || qs + 31 >= T) {
+    if (qs < kw + 16 * KB - 1 || qs + 31 >= T) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int kb2 = 0; kb2 < KB; ++kb2)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int qi = qs + 16 * t + 4 * g + j;
-          if (qi < my_k || qi >= T) sacc[t][j] = -INFINITY;
-        }
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int qi = qs + 16 * t + 4 * g + j;
+            if (qi < kw + 16 * kb2 + c || qi >= T) sacc[kb2][t][j] = -INFINITY;
+          }
     }
-    f16x8 pop, dsop, drop;
+    f16x8 pop[KB], dsop[KB], drop[KB];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int r0 = 32 * st + 16 * t + 4 * g;
@@ -936,15 +975,17 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) rs[j] = *reinterpret_cast<const f32x4*>(&sm.sc[buf][r0 + j][0]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p = fast_exp2(__builtin_fmaf(sacc[t][j], scale_log2, -rs[j][0]));
-        const float r = racc[t][j], A = aacc[t][j];
-        // with f = 1 + c - r:  dS = p [f A + delta r - (G + delta c)],  dR = p (delta - A)
-        const float f = rs[j][1] - r;
-        pop[4 * t + j] = (_Float16)(p * f);
-        dsop[4 * t + j] = (_Float16)((scale * p) * __builtin_fmaf(A, f, __builtin_fmaf(r, rs[j][3], -rs[j][2])));
-        drop[4 * t + j] = (_Float16)(p * (rs[j][3] - A));
-      }
+      for (int kb2 = 0; kb2 < KB; ++kb2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = fast_exp2(__builtin_fmaf(sacc[kb2][t][j], scale_log2, -rs[j][0]));
+          const float r = racc[kb2][t][j], A = aacc[kb2][t][j];
+          // with f = 1 + c - r:  dS = p [f A + delta r - (G + delta c)],  dR = p (delta - A)
+          const float f = rs[j][1] - r;
+          pop[kb2][4 * t + j] = (_Float16)(p * f);
+          dsop[kb2][4 * t + j] = (_Float16)((scale * p) * __builtin_fmaf(A, f, __builtin_fmaf(r, rs[j][3], -rs[j][2])));
+          drop[kb2][4 * t + j] = (_Float16)(p * (rs[j][3] - A));
+        }
     }
     // gradient MFMAs: A = Q^T / rho^T / dO^T, 16 d rows x 32 queries each
     unsigned tq = lds_addr(&sm.q[buf][(32 * st + 4 * g + (c >> 2)) * SM::LD + 4 * (c & 3)]);
@@ -958,9 +999,12 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
       const f16x8 aq = __builtin_shufflevector(tr16_at(tq + o0), tr16_at(tq + o1), 0, 1, 2, 3, 4, 5, 6, 7);
       const f16x8 ar = __builtin_shufflevector(tr16_at(tr + o0), tr16_at(tr + o1), 0, 1, 2, 3, 4, 5, 6, 7);
       const f16x8 ag = __builtin_shufflevector(tr16_at(tg + o0), tr16_at(tg + o1), 0, 1, 2, 3, 4, 5, 6, 7);
-      dva[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ag, pop, dva[dt], 0, 0, 0);
-      dka[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, dsop, dka[dt], 0, 0, 0);
-      dka[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ar, drop, dka[dt], 0, 0, 0);
+#pragma unroll
+      for (int kb2 = 0; kb2 < KB; ++kb2) {
+        dva[kb2][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ag, pop[kb2], dva[kb2][dt], 0, 0, 0);
+        dka[kb2][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, dsop[kb2], dka[kb2][dt], 0, 0, 0);
+        dka[kb2][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ar, drop[kb2], dka[kb2][dt], 0, 0, 0);
+      }
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -983,20 +1027,24 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv16b_kernel(
     if (n + 1 < ntile) iter(n + 1, 1);
   }
 
-  // dka[dt][jj] is d = 16 dt + 4 g + jj of key c; the sums ran on s dO
-  if (kvalid) {
-    float* dkr = dk + (kvbase + my_k) * D;
-    float* dvr = dv + (kvbase + my_k) * D;
+  // dka[kb2][dt][jj] is d = 16 dt + 4 g + jj of key kw + 16 kb2 + c; the sums ran on s dO
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      f32x4 x, y;
+  for (int kb2 = 0; kb2 < KB; ++kb2) {
+    const int my_k = kw + 16 * kb2 + c;
+    if (my_k < T) {
+      float* dkr = dk + (kvbase + my_k) * D;
+      float* dvr = dv + (kvbase + my_k) * D;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        x[jj] = ginv * dka[dt][jj];
-        y[jj] = ginv * dva[dt][jj];
+      for (int dt = 0; dt < ND; ++dt) {
+        f32x4 x, y;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          x[jj] = ginv * dka[kb2][dt][jj];
+          y[jj] = ginv * dva[kb2][dt][jj];
+        }
+        *reinterpret_cast<f32x4*>(dkr + 16 * dt + 4 * g) = x;
+        *reinterpret_cast<f32x4*>(dvr + 16 * dt + 4 * g) = y;
       }
-      *reinterpret_cast<f32x4*>(dkr + 16 * dt + 4 * g) = x;
-      *reinterpret_cast<f32x4*>(dvr + 16 * dt + 4 * g) = y;
     }
   }
 }
@@ -1035,14 +1083,16 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
     }
     // waves per workgroup and tile sizes: see DqbSmem
     constexpr int NW = D > 128 ? 4 : 8, BC = D > 128 ? 32 : 128, BQ = D > 128 ? 32 : 64;
-    const int nqb16 = (T + 16 * NW - 1) / (16 * NW);
-    const int nkb16 = (T + 16 * NW - 1) / (16 * NW);
-    hipLaunchKernelGGL((bwd_dq16b_kernel<D, NW, BC>), dim3(nqb16 * B * Hq), dim3(64 * NW), 0, stream,
+    constexpr int QB = D == 64 ? PLX_QB64 : 1;  // query blocks per dQ wave
+    const int nqb16 = (T + 16 * NW * QB - 1) / (16 * NW * QB);
+    constexpr int KB = D == 64 ? PLX_KB64 : 1;  // key blocks per dK/dV wave
+    const int nkb16 = (T + 16 * NW * KB - 1) / (16 * NW * KB);
+    hipLaunchKernelGGL((bwd_dq16b_kernel<D, NW, BC, QB>), dim3(nqb16 * B * Hq), dim3(64 * NW), 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k16, (const uint16_t*)v,
                        (const uint16_t*)rho, (const uint16_t*)d_o, o, vbar, lse, c_aux, G, dl, q16,
                        r16, g16, dsc, dq, drho, B, Hq, Hkv, T, scale, scale * kLog2e);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv16b_kernel<D, NW, BQ>), dim3(nkb16 * B * Hkv), dim3(64 * NW), 0, stream,
+    hipLaunchKernelGGL((bwd_dkdv16b_kernel<D, NW, BQ, KB>), dim3(nkb16 * B * Hkv), dim3(64 * NW), 0, stream,
                        (const uint16_t*)q16, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)r16, (const uint16_t*)g16, lse, c_aux, G, dl, dsc, dk, dv, B,
                        Hq, Hkv, T, scale, scale * kLog2e);
