@@ -17,8 +17,9 @@
 // (global_load_lds, no register staging) in an XOR-swizzled layout that keeps
 // the operand reads free of bank conflicts; tile t+1 is requested at the
 // start of tile t.  The operands of each 32-deep step are read from LDS while
-// the previous step's MFMAs run; at a tile boundary the barrier and the first
-// reads of the next tile sit before the last step's MFMAs.  The epilogue
+// the previous step's MFMAs run, in two groups between them (the tile loads
+// likewise); at a tile boundary the barrier and the first reads of the next
+// tile sit before the last step's MFMAs.  The epilogue
 // rounds to bf16 (round to nearest even), transposes each wave's tile through
 // LDS and stores whole rows of d, one head per 16-lane group.
 #include "plx_common.hpp"
@@ -122,30 +123,41 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_kernel(
   __syncthreads();
   Ops cur, nxt;
   read_ops(cur, 0, 0);
+  static_assert(PJ_BK == 64, "two 32-deep steps per tile");
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    const bool more = t + 1 < ntiles;
-    // tile t+1 into the other buffer, whose tile t-1 every wave finished
-    // reading before the barrier that ended tile t-1
-    if (more) gload(buf ^ 1, (t + 1) * PJ_BK);
+    // step 0: tile t+1 into the other buffer (whose tile t-1 every wave
+    // finished reading before the barrier that ended tile t-1; the last tile
+    // reloads itself there, which keeps the block free of branches) and the
+    // operands of step 1, issued in two groups between the MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+    gload(buf ^ 1, min(t + 1, ntiles - 1) * PJ_BK);
+    read_ops(nxt, buf, 1);
+    mfmas(cur);
 #pragma unroll
-    for (int ks = 0; ks < PJ_BK / 32 - 1; ++ks) {
-      read_ops(nxt, buf, ks + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(cur);
-      __builtin_amdgcn_sched_barrier(0);
-      cur = nxt;
+    for (int r = 0; r < 2; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);   // global loads
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMAs
     }
-    // last step: wait for tile t+1, make it visible, start reading it, then
-    // issue this step's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+    cur = nxt;
+    // step 1: wait for tile t+1, make it visible, read its first operands
+    // between this step's MFMAs
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (more) read_ops(nxt, buf ^ 1, 0);
     __builtin_amdgcn_sched_barrier(0);
+    read_ops(nxt, buf ^ 1, 0);
     mfmas(cur);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     cur = nxt;
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // every wave is done with the operand buffers
 
   // epilogue: acc[i][j][r] is feature wn*128 + 16 i + 4 g + r and token
