@@ -597,60 +597,60 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq16b_kernel(
   float lse2[QB], di[QB], k1[QB], k2[QB];
 #pragma unroll
   for (int qb2 = 0; qb2 < QB; ++qb2) {
-  const int my_q = qw + 16 * qb2 + c;
-  const bool qvalid = my_q < T;
-  float Gi = 0.f, dd = 0.f;
+    const int my_q = qw + 16 * qb2 + c;
+    const bool qvalid = my_q < T;
+    float Gi = 0.f, dd = 0.f;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4 qa = {0u, 0u, 0u, 0u}, ra = qa, ga = qa;
-    if (qvalid) {
-      const size_t off = (rowbase + my_q) * D + 32 * s + 8 * g;
-      qa = *reinterpret_cast<const u32x4*>(q + off);
-      ra = *reinterpret_cast<const u32x4*>(rho + off);
-      ga = *reinterpret_cast<const u32x4*>(d_o + off);
-      // s dO is exact in bf16 (a power of two moves only the exponent)
+    for (int s = 0; s < NS; ++s) {
+      u32x4 qa = {0u, 0u, 0u, 0u}, ra = qa, ga = qa;
+      if (qvalid) {
+        const size_t off = (rowbase + my_q) * D + 32 * s + 8 * g;
+        qa = *reinterpret_cast<const u32x4*>(q + off);
+        ra = *reinterpret_cast<const u32x4*>(rho + off);
+        ga = *reinterpret_cast<const u32x4*>(d_o + off);
+        // s dO is exact in bf16 (a power of two moves only the exponent)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = __builtin_bit_cast(float, ga[e] << 16) * gsc;
-        const float hi = __builtin_bit_cast(float, ga[e] & 0xffff0000u) * gsc;
-        ga[e] = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xffff0000u);
+        for (int e = 0; e < 4; ++e) {
+          const float lo = __builtin_bit_cast(float, ga[e] << 16) * gsc;
+          const float hi = __builtin_bit_cast(float, ga[e] & 0xffff0000u) * gsc;
+          ga[e] = (__builtin_bit_cast(uint32_t, lo) >> 16) | (__builtin_bit_cast(uint32_t, hi) & 0xffff0000u);
+        }
+        const f32x4 o0 = *reinterpret_cast<const f32x4*>(o + off);
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(o + off + 4);
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(vbar + off);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(vbar + off + 4);
+        const u16x8 gb = __builtin_bit_cast(u16x8, ga);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = bf16_bits_to_f32(gb[e]), x1 = bf16_bits_to_f32(gb[4 + e]);
+          Gi = __builtin_fmaf(x0, o0[e], __builtin_fmaf(x1, o1[e], Gi));
+          dd = __builtin_fmaf(x0, v0[e], __builtin_fmaf(x1, v1[e], dd));
+        }
       }
-      const f32x4 o0 = *reinterpret_cast<const f32x4*>(o + off);
-      const f32x4 o1 = *reinterpret_cast<const f32x4*>(o + off + 4);
-      const f32x4 v0 = *reinterpret_cast<const f32x4*>(vbar + off);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(vbar + off + 4);
-      const u16x8 gb = __builtin_bit_cast(u16x8, ga);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = bf16_bits_to_f32(gb[e]), x1 = bf16_bits_to_f32(gb[4 + e]);
-        Gi = __builtin_fmaf(x0, o0[e], __builtin_fmaf(x1, o1[e], Gi));
-        dd = __builtin_fmaf(x0, v0[e], __builtin_fmaf(x1, v1[e], dd));
+      qop[qb2][s] = cvt_bf16x8_f16(qa);
+      rop[qb2][s] = cvt_bf16x8_f16(ra);
+      gop[qb2][s] = __builtin_bit_cast(bf16x8, ga);
+      if (qvalid) {
+        const size_t off = (rowbase + my_q) * D + 32 * s + 8 * g;
+        *reinterpret_cast<f16x8*>(q16 + off) = qop[qb2][s];
+        *reinterpret_cast<f16x8*>(r16 + off) = rop[qb2][s];
+        *reinterpret_cast<f16x8*>(g16 + off) = cvt_bf16x8_f16(ga);
       }
     }
-    qop[qb2][s] = cvt_bf16x8_f16(qa);
-    rop[qb2][s] = cvt_bf16x8_f16(ra);
-    gop[qb2][s] = __builtin_bit_cast(bf16x8, ga);
-    if (qvalid) {
-      const size_t off = (rowbase + my_q) * D + 32 * s + 8 * g;
-      *reinterpret_cast<f16x8*>(q16 + off) = qop[qb2][s];
-      *reinterpret_cast<f16x8*>(r16 + off) = rop[qb2][s];
-      *reinterpret_cast<f16x8*>(g16 + off) = cvt_bf16x8_f16(ga);
+    // the four 16-lane groups hold disjoint quarters of the row
+    Gi += __shfl_xor(Gi, 16, 64);
+    Gi += __shfl_xor(Gi, 32, 64);
+    dd += __shfl_xor(dd, 16, 64);
+    dd += __shfl_xor(dd, 32, 64);
+    if (qvalid && g == 0) {
+      Gv[rowbase + my_q] = Gi;
+      dlt[rowbase + my_q] = dd;
     }
-  }
-  // the four 16-lane groups hold disjoint quarters of the row
-  Gi += __shfl_xor(Gi, 16, 64);
-  Gi += __shfl_xor(Gi, 32, 64);
-  dd += __shfl_xor(dd, 16, 64);
-  dd += __shfl_xor(dd, 32, 64);
-  if (qvalid && g == 0) {
-    Gv[rowbase + my_q] = Gi;
-    dlt[rowbase + my_q] = dd;
-  }
-  lse2[qb2] = qvalid ? lse[rowbase + my_q] * kLog2e : 0.f;
-  const float ci = qvalid ? c_aux[rowbase + my_q] : 0.f;
-  di[qb2] = dd;
-  k1[qb2] = 1.f + ci;
-  k2[qb2] = Gi + dd * ci;
+    lse2[qb2] = qvalid ? lse[rowbase + my_q] * kLog2e : 0.f;
+    const float ci = qvalid ? c_aux[rowbase + my_q] : 0.f;
+    di[qb2] = dd;
+    k1[qb2] = 1.f + ci;
+    k2[qb2] = Gi + dd * ci;
   }  // query blocks
   lds_put(0);
   __syncthreads();
