@@ -93,3 +93,78 @@ def test_prefill_graph_replays_match_eager(gpu_lib):
         torch.cuda.synchronize()
         assert torch.equal(got, o), f"replay {rep} differs from eager"
     del g
+
+
+def test_bwd_graph_replays_match_eager(gpu_lib):
+    """The bf16 backward (dO scale reduction, its scale, dQ/drho, dK/dV) in one
+    graph: each replay takes the dO in memory at replay time, including its
+    power-of-two scale, and matches the eager call bit for bit."""
+    import torch
+
+    from parallax_local_linear_plx_amd import bwd_workspace_size, plx_bwd, plx_fwd_prefill
+
+    B, Hq, Hkv, T, d = 1, 4, 2, 300, 128
+    say(f"case bwd graph replay B{B} Hq{Hq} Hkv{Hkv} T{T} d{d}")
+    wl = inputs.make_prefill(B, Hq, Hkv, T, d, dtype="bf16", seed=122, with_grad=True)
+    t = {n: to_device(x).clone() for n, x in wl.tensors.items()}
+    fwd = plx_fwd_prefill(t["q"], t["k"], t["v"], t["rho"], wl.scale, aux=True)
+    ws = torch.empty(bwd_workspace_size(B, Hq, Hkv, T, d), dtype=torch.uint8, device="cuda")
+    grads = {n: torch.empty(shape, dtype=torch.float32, device="cuda")
+             for n, shape in (("dq", (B, Hq, T, d)), ("dk", (B, Hkv, T, d)), ("dv", (B, Hkv, T, d)),
+                              ("drho", (B, Hq, T, d)))}
+    d_o = t["d_o"]
+    base = d_o.clone()
+
+    def call():
+        plx_bwd(t["q"], t["k"], t["v"], t["rho"], d_o, fwd["o"], fwd["lse"], fwd["c"], fwd["vbar"], wl.scale,
+                workspace=ws, grads=grads)
+
+    g = _capture(call)
+    for rep, sc in enumerate((1.0, 2.0 ** -20, 2.0 ** 12, 1.0)):
+        d_o.copy_(base * sc)  # exact in bf16: a power of two
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = {n: x.clone() for n, x in grads.items()}
+        ws.fill_(0xFF)  # eager work between replays, and a dirty workspace
+        for x in grads.values():
+            x.zero_()
+        call()
+        torch.cuda.synchronize()
+        for n, x in grads.items():
+            assert torch.equal(got[n], x), f"replay {rep} (dO x {sc}) differs from eager in {n}"
+    del g
+
+
+def test_projection_graph_replays_match_eager(gpu_lib):
+    import torch
+
+    from parallax_local_linear_plx_amd import plx_qkvr_proj
+
+    B, T, D, Hq, Hkv, d = 2, 300, 256, 4, 2, 64
+    say(f"case projection graph replay B{B} T{T} D{D} Hq{Hq} Hkv{Hkv} d{d}")
+    wl = inputs.make_projection(B, T, D, Hq, Hkv, d, seed=123)
+    x = to_device(wl.tensors["x"]).clone()
+    w = to_device(wl.tensors["w"]).clone()
+    out = {n: torch.empty((B, H, T, d), dtype=torch.bfloat16, device="cuda")
+           for n, H in (("q", Hq), ("k", Hkv), ("v", Hkv), ("rho", Hq))}
+
+    def call():
+        plx_qkvr_proj(x, w, Hq, Hkv, d, out=out)
+
+    g = _capture(call)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    for rep in range(3):
+        x.copy_(torch.randn(x.shape, generator=gen, device="cuda").bfloat16())
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = {n: y.clone() for n, y in out.items()}
+        for y in out.values():
+            y.zero_()
+        call()
+        torch.cuda.synchronize()
+        for n, y in out.items():
+            assert torch.equal(got[n], y), f"replay {rep} differs from eager in {n}"
+    del g
