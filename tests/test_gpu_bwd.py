@@ -80,6 +80,8 @@ def test_fp32_gradients(gpu_lib, B, Hq, Hkv, T, d):
     (1, 8, 2, 513, 64),    # G = 4; several 128-key blocks and 64-row query tiles, ragged tail
     (1, 16, 1, 200, 128),  # G = 16: one KV head shared by sixteen query heads
     (1, 6, 2, 150, 64),    # G = 3
+    (1, 2, 1, 17, 64),     # d = 64 waves hold two 16-row blocks: the second holds one row
+    (1, 4, 2, 257, 64),    # one row past the 256 rows (and keys) of a d = 64 workgroup
 ])
 def test_bf16_gradients(gpu_lib, B, Hq, Hkv, T, d):
     """Training-workload probe scale, rho ~ N(0, 0.1^2): the bf16 bars."""
