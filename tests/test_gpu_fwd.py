@@ -56,6 +56,9 @@ def test_fp32_gqa_ragged(gpu_lib, B, Hq, Hkv, T, d):
     (2, 2, 1, 64, 128, False),
     (1, 1, 1, 1, 128, True),
     (1, 6, 2, 150, 128, False),  # three query heads per KV head
+    (1, 1, 1, 1, 64, False),     # d = 64 waves hold two 16-row blocks: a single row
+    (1, 2, 1, 17, 64, True),     # the second block of a wave holds one row
+    (1, 4, 2, 257, 64, False),   # one row past the 256 rows of a d = 64 workgroup
 ])
 def test_bf16_against_oracle(gpu_lib, B, Hq, Hkv, T, d, proj):
     say(f"case bf16 B{B} Hq{Hq} Hkv{Hkv} T{T} d{d} projected-rho={proj}")
