@@ -417,6 +417,9 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void bwd_dkdv_kernel(
 // exact, so the result does not depend on the scale of dO except through
 // fp32 underflow or overflow of the gradients themselves.
 inline size_t bwd_ws_align(size_t n) { return (n + 255) & ~(size_t)255; }
+// 16-key blocks per dK/dV wave and 16-row blocks per dQ wave at d = 64 (one
+// block each at d = 128 and 256, where the registers hold no second block);
+// 1 builds the one-block kernels, which give the same gradients bit for bit.
 #ifndef PLX_KB64
 #define PLX_KB64 2
 #endif
