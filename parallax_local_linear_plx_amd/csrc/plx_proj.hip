@@ -19,9 +19,11 @@
 // start of tile t.  The operands of each 32-deep step are read from LDS while
 // the previous step's MFMAs run, in two groups between them (the tile loads
 // likewise); at a tile boundary the barrier and the first reads of the next
-// tile sit before the last step's MFMAs.  The epilogue
-// rounds to bf16 (round to nearest even), transposes each wave's tile through
-// LDS and stores whole rows of d, one head per 16-lane group.
+// tile sit before the last step's MFMAs.  The epilogue rounds to bf16 (round
+// to nearest even) and stores straight from the accumulators: two permlane16
+// swaps per pair of 16-feature blocks give each lane 8 adjacent features of
+// one token, so the four lanes of a token write 64 contiguous bytes of one
+// head's d-row (no LDS round trip, no barrier).
 #include "plx_common.hpp"
 #include "plx_kernels.hpp"
 
@@ -34,18 +36,12 @@ constexpr int PJ_BN = 256;      // output features per workgroup
 constexpr int PJ_BK = 64;       // reduction depth of one LDS tile
 constexpr int PJ_THREADS = 512;
 constexpr int PJ_LD = PJ_BK;  // LDS row stride (elements): 128 B, chunks XOR-swizzled
-constexpr int PJ_OLD = 128 + 8;   // epilogue row stride (elements)
 // the loads cover a tile as 8 waves x 4 instructions x 8 rows
 static_assert(PJ_THREADS / 64 * 4 * 8 == PJ_BM && PJ_BM == PJ_BN, "tile load coverage");
 
 struct ProjSmem {
-  union {
-    struct {
-      uint16_t w[2][PJ_BN * PJ_LD];
-      uint16_t x[2][PJ_BM * PJ_LD];
-    } in;
-    uint16_t out[8][64 * PJ_OLD];  // one 64 x 128 bf16 tile per wave
-  };
+  uint16_t w[2][PJ_BN * PJ_LD];
+  uint16_t x[2][PJ_BM * PJ_LD];
 };
 
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
@@ -83,9 +79,9 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_kernel(
       const uint16_t* gw = w + (size_t)min(n0 + row, N - 1) * K + k0 + 8 * lc;
       const uint16_t* gx = x + (size_t)min(m0 + row, M - 1) * K + k0 + 8 * lc;
       __builtin_amdgcn_global_load_lds((const void*)gw,
-          (__attribute__((address_space(3))) void*)&sm.in.w[buf][blk * 8 * PJ_LD], 16, 0, 0);
+          (__attribute__((address_space(3))) void*)&sm.w[buf][blk * 8 * PJ_LD], 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)gx,
-          (__attribute__((address_space(3))) void*)&sm.in.x[buf][blk * 8 * PJ_LD], 16, 0, 0);
+          (__attribute__((address_space(3))) void*)&sm.x[buf][blk * 8 * PJ_LD], 16, 0, 0);
     }
   };
   // operands of one 32-deep step: A = W rows (features), B = X rows (tokens);
@@ -96,8 +92,8 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_kernel(
   const int swz = (c16 >> 1) & 7;
   auto read_ops = [&](Ops& o, int buf, int ks) {
     const int pc = (4 * ks + g4) ^ swz;
-    const uint16_t* wr = &sm.in.w[buf][(wn * 128 + c16) * PJ_LD + 8 * pc];
-    const uint16_t* xr = &sm.in.x[buf][(wm * 64 + c16) * PJ_LD + 8 * pc];
+    const uint16_t* wr = &sm.w[buf][(wn * 128 + c16) * PJ_LD + 8 * pc];
+    const uint16_t* xr = &sm.x[buf][(wm * 64 + c16) * PJ_LD + 8 * pc];
 #pragma unroll
     for (int i = 0; i < 8; ++i) o.a[i] = *reinterpret_cast<const bf16x8*>(wr + 16 * i * PJ_LD);
 #pragma unroll
@@ -158,48 +154,54 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_kernel(
     cur = nxt;
   }
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // every wave is done with the operand buffers
-
-  // epilogue: acc[i][j][r] is feature wn*128 + 16 i + 4 g + r and token
-  // wm*64 + 16 j + c; round to bf16 and transpose through LDS
-  uint16_t* ot = sm.out[wave];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int nl = 16 * i + 4 * g4, ml = 16 * j + c16;
-      uint2 pk;
-      pk.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-      pk.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-      *reinterpret_cast<uint2*>(&ot[ml * PJ_OLD + nl]) = pk;
-    }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  // 16 lanes per token row, 8 features each: a head's whole d-row per group
+  // epilogue from registers: acc[i][j][r] is feature wn*128 + 16 i + 4 g + r
+  // of token wm*64 + 16 j + c; two permlane16 swaps per pair of feature
+  // blocks (2p, 2p+1) leave in lane (c, g) the 8 adjacent features
+  // 16 (2p + g % 2) + 8 (g / 2) .. + 7 of token c: 64 contiguous bytes of
+  // one head's d-row per token and store
   const int nq = Hq * d, nk = nq + Hkv * d, nv = nk + Hkv * d;
-#pragma unroll 4
-  for (int i = 0; i < 64 * 16 / 64; ++i) {
-    const int it = 64 * i + lane;
-    const int row = it >> 4, c = (it & 15) * 8;
-    const int m = m0 + wm * 64 + row, n = n0 + wn * 128 + c;
-    if (m >= M || n >= N) continue;
-    const u32x4 val = *reinterpret_cast<const u32x4*>(&ot[row * PJ_OLD + c]);
+  int bj[4];
+  size_t tok[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = min(m0 + wm * 64 + 16 * j + c16, M - 1);
+    bj[j] = m / T;
+    tok[j] = (size_t)(m - bj[j] * T) * d;
+  }
+  const int lf = 16 * (g4 & 1) + 8 * (g4 >> 1);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int nb = n0 + wn * 128 + 32 * p;  // one tensor and head for these 32 features
+    if (nb >= N) continue;
     uint16_t* base;
     int H, loc;
-    if (n < nq) {
-      base = q, H = Hq, loc = n;
-    } else if (n < nk) {
-      base = k, H = Hkv, loc = n - nq;
-    } else if (n < nv) {
-      base = v, H = Hkv, loc = n - nk;
+    if (nb < nq) {
+      base = q, H = Hq, loc = nb;
+    } else if (nb < nk) {
+      base = k, H = Hkv, loc = nb - nq;
+    } else if (nb < nv) {
+      base = v, H = Hkv, loc = nb - nk;
     } else {
-      base = rho, H = Hq, loc = n - nv;
+      base = rho, H = Hq, loc = nb - nv;
     }
-    const int b = m / T, tt = m - b * T;
     const int head = loc / d, dd = loc - head * d;
-    *reinterpret_cast<u32x4*>(base + (((size_t)b * H + head) * T + tt) * d + dd) = val;
+    uint16_t* hb = base + (size_t)head * T * d + dd + lf;
+    const size_t bstride = (size_t)H * T * d;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 ea = acc[2 * p][j], eb = acc[2 * p + 1][j];
+      const unsigned a0 = pack_bf16x2(ea[0], ea[1]), a1 = pack_bf16x2(ea[2], ea[3]);
+      const unsigned b0 = pack_bf16x2(eb[0], eb[1]), b1 = pack_bf16x2(eb[2], eb[3]);
+      const auto s0 = __builtin_amdgcn_permlane16_swap(a0, b0, false, false);
+      const auto s1 = __builtin_amdgcn_permlane16_swap(a1, b1, false, false);
+      u32x4 val;
+      val[0] = s0[0];
+      val[1] = s1[0];
+      val[2] = s0[1];
+      val[3] = s1[1];
+      if (m0 + wm * 64 + 16 * j + c16 < M)
+        *reinterpret_cast<u32x4*>(hb + bj[j] * bstride + tok[j]) = val;
+    }
   }
 }
 
